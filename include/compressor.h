@@ -1,0 +1,215 @@
+/*
+ * compressor.h - C ABI of the MI355X (gfx950) Compressor library.
+ *
+ * The operator is the DeepSeek-V4 KV Compressor: every `ratio` tokens of
+ * hidden states become one compressed KV row.  Definitions cited below:
+ *   [PyPTO]   page "CANN PyPTO 算子实战：Compressor 长序列 KV Cache 压缩算子的原理、参数与调用方法"
+ *   [CANN]    page "compressor-算子接口（torch_extension）-算子库-API参考-CANN9.2.0-beta.1开发文档"
+ *   [AscendC] page "NPU DeepSeek-V4 Ascend C 融合算子优化", section Compressor
+ *   [Triton]  the 10100.com article on the Triton-Ascend Compressor (CANNBot
+ *             triton-op-generator)
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Pointers marked (device) are HIP device addresses on the current device;
+ *   (host) are host addresses.  The caller owns every buffer; the library
+ *   never allocates device memory during a call and keeps no pointer after
+ *   the work it enqueued has finished.
+ * - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *   Work is enqueued asynchronously; no call synchronises the host except
+ *   compressor_last_device_error and compressor_timing_query.
+ * - bf16 buffers hold raw bfloat16 values (2 bytes each), row-major and
+ *   contiguous; fp32 and int32 likewise.
+ * - Return value: a compressor_status.  Host-checkable argument errors are
+ *   reported before anything is enqueued.  Value errors only visible on the
+ *   device (bad table entries, negative start_pos, seqused beyond its slot,
+ *   more output rows than out_rows) never cause an out-of-bounds access: the
+ *   offending access is skipped and a bit is set in the workspace's error
+ *   word, read with compressor_last_device_error.
+ * - Calls are deterministic: no floating-point atomics, fixed reduction order
+ *   ([CANN] 约束说明: deterministic computation by default).
+ */
+#ifndef COMPRESSOR_H_
+#define COMPRESSOR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (after the aclnn NULLPTR / PARAM_INVALID / TILING_ERROR
+ * convention of the NsaCompressWithCache page). */
+typedef enum {
+  CMP_OK = 0,
+  CMP_ERR_NULLPTR = 1,      /* a required pointer is NULL */
+  CMP_ERR_INVALID = 2,      /* shape or range violation */
+  CMP_ERR_UNSUPPORTED = 3,  /* configuration outside the supported set */
+  CMP_ERR_WORKSPACE = 4,    /* workspace_bytes below compressor_*_workspace_size */
+  CMP_ERR_OUT_ROWS = 5,     /* out_rows below what the call may write */
+  CMP_ERR_HIP = 6           /* a HIP runtime call failed */
+} compressor_status;
+
+/* Bits of the device error word. */
+#define CMP_DEVERR_TABLE 1u      /* block-table entry outside [0, num_blocks) */
+#define CMP_DEVERR_START_POS 2u  /* start_pos < 0: request treated as empty */
+#define CMP_DEVERR_SEQLEN 4u     /* cu_seqlens not monotone / beyond T, or seqused outside [0, slot] */
+#define CMP_DEVERR_OUT_ROWS 8u   /* sum over requests of ceil(n_b / ratio) > out_rows */
+
+/*
+ * Static shape of a Compressor layer.
+ *
+ * ratio         r, tokens per compressed row: 4 or 128 ([CANN] 约束说明 lists
+ *               the C4A / C4Li / C128A combinations).  coff, the number of
+ *               channel sets, is 2 for ratio 4 and 1 otherwise ([PyPTO] 参数说明).
+ * head_dim      D: 128 or 512.
+ * hidden        H: multiple of 512 in [1024, 10240].
+ * rope_head_dim 64 (the only supported value, [PyPTO] 参数说明).
+ * rotate        nonzero: multiply the result by the D x D Hadamard matrix.
+ * block_size    rows per state block, 1..1024.
+ * num_blocks    blocks in each state pool.
+ * table_stride  int32 entries per block-table row; >= ceil(coff*r / block_size).
+ */
+typedef struct {
+  int32_t ratio;
+  int32_t head_dim;
+  int32_t hidden;
+  int32_t rope_head_dim;
+  int32_t rotate;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t table_stride;
+} compressor_shape;
+
+/*
+ * Arguments of one prefill or decode call.
+ *
+ * x                 (device) bf16 [T, H]: packed hidden states of all requests.
+ * T, batch          packed rows and number of requests B (B >= 1; T == 0 is a
+ *                   valid call that only zero-fills out).
+ * cu_seqlens        (device) int32 [B+1] or NULL: request b's slot is rows
+ *                   [cu[b], cu[b+1]) of x; NULL means B equal slots of T/B rows
+ *                   (x given as [B, S, H]).  Decode requires NULL.
+ * seqused           (device) int32 [B] or NULL: valid tokens of request b, the
+ *                   first seqused[b] rows of its slot ([Triton] varlen packing
+ *                   with cu_seqlens and seqused).  NULL: the whole slot.
+ * start_pos         (device) int32 [B] or NULL: position of request b's first
+ *                   token in this call; NULL means 0 ([PyPTO] 参数说明).
+ * kv_state,         (device) fp32 [num_blocks, block_size, coff*D], updated in
+ * score_state       place.  Request b keeps a ring of coff*r rows: position p
+ *                   lives in ring slot q = p mod (coff*r), at block
+ *                   table[b*table_stride + q / block_size], row q % block_size.
+ *                   Rows hold all coff*D channels of kv (resp. score incl. Ape).
+ *                   After a call, exactly the rows of positions
+ *                   [max(s, r*floor(e/r) - (coff-1)*r), e) of this call are
+ *                   stored (e = s + n); no other row changes.  Requests must
+ *                   not share blocks.
+ * kv_block_table    (device) int32 [B, table_stride] addressing kv_state, or
+ *                   NULL to use state_block_table for both pools.
+ * state_block_table (device) int32 [B, table_stride] addressing score_state.
+ * w_packed          (device) bf16 [2*coff*D, H], written once per weight set by
+ *                   compressor_pack_weights from wkv and wgate.
+ * ape               (device) fp32 [r, coff*D]: positional bias added to the
+ *                   score of position p from row p mod r.
+ * norm_weight       (device) bf16 [D]: RMSNorm weight (epsilon 1e-6).
+ * hadamard          (device) bf16 [D, D], required iff rotate: out = y @ hadamard.
+ * sin, cos          (device) bf16 [out_rows, rope_head_dim]: row i rotates
+ *                   output row i; column i drives the even element of pair i,
+ *                   column rope_head_dim/2 + i the odd one.
+ * out               (device) bf16 [out_rows, D].  Request b owns rows
+ *                   [o_b, o_b + ceil(n_b/r)), o_b = sum of earlier requests'
+ *                   counts; its k-th completed window is row o_b + k; every
+ *                   other row (windows not completed, rows past the last
+ *                   request) is +0.0 ([PyPTO] 返回值说明: shape
+ *                   [min(T, T//ratio + B), D], zero where nothing compresses).
+ * workspace         (device) scratch of at least workspace_bytes, sized by
+ *                   compressor_prefill_workspace_size / _decode_; it also holds
+ *                   the device error word of the last call.  Calls sharing a
+ *                   workspace must be ordered on one stream.
+ */
+typedef struct {
+  const void* x;
+  int32_t T;
+  int32_t batch;
+  const int32_t* cu_seqlens;
+  const int32_t* seqused;
+  const int32_t* start_pos;
+  float* kv_state;
+  float* score_state;
+  const int32_t* kv_block_table;
+  const int32_t* state_block_table;
+  const void* w_packed;
+  const float* ape;
+  const void* norm_weight;
+  const void* hadamard;
+  const void* sin;
+  const void* cos;
+  void* out;
+  int32_t out_rows;
+  void* workspace;
+  size_t workspace_bytes;
+} compressor_args;
+
+/* Workspace bytes a prefill call with T packed rows, `batch` requests and
+ * out_rows output rows needs (host only, no device work). */
+int compressor_prefill_workspace_size(const compressor_shape* shape, int32_t T, int32_t batch,
+                                      int32_t out_rows, size_t* bytes);
+
+/* Workspace bytes a decode call with `batch` requests needs (host only). */
+int compressor_decode_workspace_size(const compressor_shape* shape, int32_t batch,
+                                     int32_t out_rows, size_t* bytes);
+
+/* Fuse wkv and wgate (device, bf16 [coff*D, H] each; [CANN] 计算公式 step 1
+ * and [AscendC] 矩阵乘法: [kv, score] = X @ [W_kv, W_gate]) into one bf16
+ * [2*coff*D, H] panel whose row order the kernels expect.  The panel's row
+ * order is internal; only compressor_* calls read it.  Enqueued on stream. */
+int compressor_pack_weights(const compressor_shape* shape, const void* wkv, const void* wgate,
+                            void* w_packed, void* stream);
+
+/* Fill both pools: kv 0, score -inf (the padding values of the first window,
+ * [PyPTO] 压缩窗口与状态更新). */
+int compressor_state_init(const compressor_shape* shape, float* kv_state, float* score_state,
+                          void* stream);
+
+/* Reset the ring blocks of n requests: rows (device, int32 [n]) are
+ * block-table row indices; every block those table rows name (first
+ * ceil(coff*r / block_size) entries) is refilled with kv 0 / score -inf. */
+int compressor_state_reset(const compressor_shape* shape, float* kv_state, float* score_state,
+                           const int32_t* kv_block_table, const int32_t* state_block_table,
+                           const int32_t* rows, int32_t n, void* stream);
+
+/* One Compressor call over packed variable-length requests ([CANN] 接口功能
+ * and 计算公式; [PyPTO] 压缩窗口与状态更新; [Triton] 流式调用).  Computes the
+ * fused projection, Ape, window pooling with the state rows of earlier calls,
+ * RMSNorm, RoPE, the optional Hadamard product, zero rows, and the state
+ * write-back described at compressor_args. */
+int compressor_prefill(const compressor_shape* shape, const compressor_args* args, void* stream);
+
+/* The same operator for one token per request ([Triton] 性能优化: decode has
+ * one token per request and different scheduling).  x is [batch, H];
+ * cu_seqlens must be NULL; seqused, if given, is 0 or 1 per request. */
+int compressor_decode(const compressor_shape* shape, const compressor_args* args, void* stream);
+
+/* Synchronise `stream`, then read the device error word (CMP_DEVERR_* bits)
+ * of the last call that used `workspace` into *code. */
+int compressor_last_device_error(const void* workspace, void* stream, int32_t* code);
+
+/* Static text of a status code. */
+const char* compressor_status_str(int status);
+
+/* Kernel timing: while enabled, every kernel the library enqueues is
+ * bracketed by a pair of HIP events on the same stream.  Enabling clears the
+ * records.  Kernel names: "plan", "gemm", "pool", "post", "writeback",
+ * "hadamard_t", "gemv", "decode_tail", "pack", "state_fill". */
+int compressor_timing_enable(int32_t on);
+
+/* Wait for the recorded events, then report the number of launches of
+ * `kernel` and the sum of their durations in milliseconds. */
+int compressor_timing_query(const char* kernel, int32_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COMPRESSOR_H_ */

@@ -1,0 +1,219 @@
+"""Python binding of the MI355X Compressor library (libcompressor.so).
+
+Argument marshalling only: torch tensors are checked for device, dtype and
+contiguity and passed to the C ABI of include/compressor.h as raw device
+pointers, together with the current HIP stream.  Every step of the operator
+runs in the library's HIP kernels; if the library is not built, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcompressor.so")
+
+CMP_OK = 0
+STATUS = {0: "CMP_OK", 1: "CMP_ERR_NULLPTR", 2: "CMP_ERR_INVALID", 3: "CMP_ERR_UNSUPPORTED",
+          4: "CMP_ERR_WORKSPACE", 5: "CMP_ERR_OUT_ROWS", 6: "CMP_ERR_HIP"}
+DEVERR_TABLE, DEVERR_START_POS, DEVERR_SEQLEN, DEVERR_OUT_ROWS = 1, 2, 4, 8
+
+EXPORTS = ("compressor_prefill_workspace_size", "compressor_decode_workspace_size",
+           "compressor_pack_weights", "compressor_state_init", "compressor_state_reset",
+           "compressor_prefill", "compressor_decode", "compressor_last_device_error",
+           "compressor_status_str", "compressor_timing_enable", "compressor_timing_query")
+
+
+class CompressorError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("ratio", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("rope_head_dim", ctypes.c_int32),
+                ("rotate", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("table_stride", ctypes.c_int32)]
+
+    @property
+    def coff(self) -> int:
+        return 2 if self.ratio == 4 else 1
+
+
+class Args(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("T", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("cu_seqlens", ctypes.c_void_p), ("seqused", ctypes.c_void_p),
+                ("start_pos", ctypes.c_void_p), ("kv_state", ctypes.c_void_p),
+                ("score_state", ctypes.c_void_p), ("kv_block_table", ctypes.c_void_p),
+                ("state_block_table", ctypes.c_void_p), ("w_packed", ctypes.c_void_p),
+                ("ape", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("hadamard", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("cos", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("out_rows", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def library():
+    """Load libcompressor.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} (run __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        sp, ap = ctypes.POINTER(Shape), ctypes.POINTER(Args)
+        sig = {
+            "compressor_prefill_workspace_size": (sp, i32, i32, i32, ctypes.POINTER(sz)),
+            "compressor_decode_workspace_size": (sp, i32, i32, ctypes.POINTER(sz)),
+            "compressor_pack_weights": (sp, vp, vp, vp, vp),
+            "compressor_state_init": (sp, vp, vp, vp),
+            "compressor_state_reset": (sp, vp, vp, vp, vp, vp, i32, vp),
+            "compressor_prefill": (sp, ap, vp),
+            "compressor_decode": (sp, ap, vp),
+            "compressor_last_device_error": (vp, vp, ctypes.POINTER(i32)),
+            "compressor_timing_enable": (i32,),
+            "compressor_timing_query": (ctypes.c_char_p, ctypes.POINTER(i32),
+                                        ctypes.POINTER(ctypes.c_double)),
+        }
+        for name, argt in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = list(argt)
+            fn.restype = ctypes.c_int
+        lib.compressor_status_str.argtypes = [ctypes.c_int]
+        lib.compressor_status_str.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != CMP_OK:
+        raise CompressorError(fn, status)
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _dev(t: Optional[torch.Tensor], dtype, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_shape(ratio: int, head_dim: int, hidden: int, rotate: bool, block_size: int,
+               num_blocks: int, table_stride: int, rope_head_dim: int = 64) -> Shape:
+    return Shape(ratio, head_dim, hidden, rope_head_dim, int(bool(rotate)), block_size,
+                 num_blocks, table_stride)
+
+
+def compressor_prefill_workspace_size(shape: Shape, T: int, batch: int, out_rows: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("compressor_prefill_workspace_size",
+           library().compressor_prefill_workspace_size(ctypes.byref(shape), T, batch, out_rows,
+                                                        ctypes.byref(n)))
+    return n.value
+
+
+def compressor_decode_workspace_size(shape: Shape, batch: int, out_rows: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("compressor_decode_workspace_size",
+           library().compressor_decode_workspace_size(ctypes.byref(shape), batch, out_rows,
+                                                      ctypes.byref(n)))
+    return n.value
+
+
+def compressor_pack_weights(shape: Shape, wkv: torch.Tensor, wgate: torch.Tensor,
+                            w_packed: torch.Tensor, stream=None) -> None:
+    bf = torch.bfloat16
+    _check("compressor_pack_weights", library().compressor_pack_weights(
+        ctypes.byref(shape), _dev(wkv, bf, "wkv"), _dev(wgate, bf, "wgate"),
+        _dev(w_packed, bf, "w_packed"), _stream(stream)))
+
+
+def compressor_state_init(shape: Shape, kv_state: torch.Tensor, score_state: torch.Tensor,
+                          stream=None) -> None:
+    f = torch.float32
+    _check("compressor_state_init", library().compressor_state_init(
+        ctypes.byref(shape), _dev(kv_state, f, "kv_state"), _dev(score_state, f, "score_state"),
+        _stream(stream)))
+
+
+def compressor_state_reset(shape: Shape, kv_state, score_state, kv_block_table,
+                           state_block_table, rows: torch.Tensor, stream=None) -> None:
+    f, i = torch.float32, torch.int32
+    _check("compressor_state_reset", library().compressor_state_reset(
+        ctypes.byref(shape), _dev(kv_state, f, "kv_state"), _dev(score_state, f, "score_state"),
+        _dev(kv_block_table, i, "kv_block_table"), _dev(state_block_table, i, "state_block_table"),
+        _dev(rows, i, "rows"), int(rows.numel()), _stream(stream)))
+
+
+def make_args(*, x, batch, kv_state, score_state, state_block_table, w_packed, ape, norm_weight,
+              sin, cos, out, workspace, cu_seqlens=None, seqused=None, start_pos=None,
+              kv_block_table=None, hadamard=None) -> Args:
+    bf, f, i = torch.bfloat16, torch.float32, torch.int32
+    if workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
+    return Args(
+        x=_dev(x, bf, "x"), T=int(x.shape[0]), batch=int(batch),
+        cu_seqlens=_dev(cu_seqlens, i, "cu_seqlens"), seqused=_dev(seqused, i, "seqused"),
+        start_pos=_dev(start_pos, i, "start_pos"), kv_state=_dev(kv_state, f, "kv_state"),
+        score_state=_dev(score_state, f, "score_state"),
+        kv_block_table=_dev(kv_block_table, i, "kv_block_table"),
+        state_block_table=_dev(state_block_table, i, "state_block_table"),
+        w_packed=_dev(w_packed, bf, "w_packed"), ape=_dev(ape, f, "ape"),
+        norm_weight=_dev(norm_weight, bf, "norm_weight"), hadamard=_dev(hadamard, bf, "hadamard"),
+        sin=_dev(sin, bf, "sin"), cos=_dev(cos, bf, "cos"), out=_dev(out, bf, "out"),
+        out_rows=int(out.shape[0]), workspace=_dev(workspace, torch.uint8, "workspace"),
+        workspace_bytes=int(workspace.numel()))
+
+
+def compressor_prefill(shape: Shape, args: Args, stream=None) -> None:
+    _check("compressor_prefill",
+           library().compressor_prefill(ctypes.byref(shape), ctypes.byref(args), _stream(stream)))
+
+
+def compressor_decode(shape: Shape, args: Args, stream=None) -> None:
+    _check("compressor_decode",
+           library().compressor_decode(ctypes.byref(shape), ctypes.byref(args), _stream(stream)))
+
+
+def compressor_last_device_error(workspace: torch.Tensor, stream=None) -> int:
+    code = ctypes.c_int32(0)
+    _check("compressor_last_device_error", library().compressor_last_device_error(
+        _dev(workspace, torch.uint8, "workspace"), _stream(stream), ctypes.byref(code)))
+    return code.value
+
+
+def compressor_status_str(status: int) -> str:
+    return library().compressor_status_str(status).decode()
+
+
+def compressor_timing_enable(on: bool) -> None:
+    _check("compressor_timing_enable", library().compressor_timing_enable(int(bool(on))))
+
+
+def compressor_timing_query(kernel: str):
+    """(launches, total milliseconds) of `kernel` since timing was enabled."""
+    n = ctypes.c_int32(0)
+    ms = ctypes.c_double(0.0)
+    _check("compressor_timing_query", library().compressor_timing_query(
+        kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value

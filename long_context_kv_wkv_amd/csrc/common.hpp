@@ -1,0 +1,85 @@
+// Device-side helpers shared by the Compressor kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "compressor.h"
+
+namespace cmp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kRmsEps = 1e-6f;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 on raw 16-bit codes
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN becomes the quiet NaN 0x7FC0.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Column order of the fused weight panel.
+//
+// The panel has N = 2*coff*D rows (one per projected column).  It is cut into
+// groups of 128 columns; a group holds 128 / (2*coff) channels, in 32-column
+// blocks: block q of a group carries variant v = q % (2*coff) of channels
+// [sub*32, sub*32 + 32) of the group, sub = q / (2*coff).  Variant v < coff
+// is kv of channel set v; variant coff + v is the score of set v.  So one
+// 32-wide MFMA column block holds 32 consecutive channels of one variant, and
+// the 2*coff variants of a channel sit in the same lane of neighbouring blocks.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int packed_col(int is_score, int cset, int c, int coff) {
+  const int nv = 2 * coff;
+  const int cpg = 128 / nv;                 // channels per 128-column group
+  const int g = c / cpg, rem = c % cpg;
+  const int sub = rem >> 5, i = rem & 31;
+  const int v = is_score ? coff + cset : cset;
+  return g * 128 + (sub * nv + v) * 32 + i;
+}
+
+// ---------------------------------------------------------------------------
+// Per-request plan record (int32 x 8) kept in the workspace.
+// ---------------------------------------------------------------------------
+enum PlanField { PL_START = 0, PL_NTOK, PL_END, PL_ROW0, PL_NWIN, PL_NROWS, PL_OUT0, PL_PAD, PL_WIDTH };
+
+// Static configuration passed by value to kernels.
+struct Cfg {
+  int ratio, coff, D, H, N, rope, rotate, bs, nblocks, stride;
+};
+
+// Ring slot of position p, and its (block, row) through a table row.
+// Returns false (and sets *bad) if the table entry is out of range.
+__device__ __forceinline__ bool state_row(const Cfg& cf, const int32_t* __restrict__ table, int b,
+                                          int p, long* row_index) {
+  const int q = p % (cf.coff * cf.ratio);
+  const int blk = table[(long)b * cf.stride + q / cf.bs];
+  if (blk < 0 || blk >= cf.nblocks) return false;
+  *row_index = (long)blk * cf.bs + (q % cf.bs);
+  return true;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ void set_error(uint32_t* err, uint32_t bits) {
+  if (bits) atomicOr(err, bits);
+}
+
+}  // namespace cmp

@@ -1,0 +1,422 @@
+// Host side of the Compressor library: argument checks, workspace layout,
+// kernel launches on the caller's stream, and the C ABI of compressor.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "compressor.h"
+#include "common.hpp"
+#include "decode.hpp"
+#include "gemm.hpp"
+#include "prefill.hpp"
+
+using namespace cmp;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// kernel timing (optional): an event pair around every launch
+// ---------------------------------------------------------------------------
+struct TimedLaunch {
+  std::string name;
+  hipEvent_t start, stop;
+};
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TimedLaunch> recs;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> spare;
+} g_timing;
+
+template <typename F>
+int launch(const char* name, hipStream_t stream, F&& fn) {
+  hipEvent_t a = nullptr, b = nullptr;
+  bool timed = false;
+  {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.on) {
+      if (!g_timing.spare.empty()) {
+        a = g_timing.spare.back().first;
+        b = g_timing.spare.back().second;
+        g_timing.spare.pop_back();
+      } else {
+        if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return CMP_ERR_HIP;
+      }
+      timed = true;
+    }
+  }
+  if (timed && hipEventRecord(a, stream) != hipSuccess) return CMP_ERR_HIP;
+  fn();
+  if (hipGetLastError() != hipSuccess) return CMP_ERR_HIP;
+  if (timed) {
+    if (hipEventRecord(b, stream) != hipSuccess) return CMP_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.recs.push_back({name, a, b});
+  }
+  return CMP_OK;
+}
+
+#define CMP_TRY(x)                  \
+  do {                              \
+    int _rc = (x);                  \
+    if (_rc != CMP_OK) return _rc;  \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// shape checks
+// ---------------------------------------------------------------------------
+int check_shape(const compressor_shape* sh, Cfg* cf) {
+  if (!sh) return CMP_ERR_NULLPTR;
+  if (sh->ratio != 4 && sh->ratio != 128) return CMP_ERR_UNSUPPORTED;
+  if (sh->head_dim != 128 && sh->head_dim != 512) return CMP_ERR_UNSUPPORTED;
+  if (sh->hidden < 1024 || sh->hidden > 10240 || sh->hidden % 512) return CMP_ERR_INVALID;
+  if (sh->rope_head_dim != 64) return CMP_ERR_UNSUPPORTED;
+  if (sh->block_size < 1 || sh->block_size > 1024) return CMP_ERR_INVALID;
+  if (sh->num_blocks < 1) return CMP_ERR_INVALID;
+  const int coff = sh->ratio == 4 ? 2 : 1;
+  if (sh->table_stride < (coff * sh->ratio + sh->block_size - 1) / sh->block_size)
+    return CMP_ERR_INVALID;
+  cf->ratio = sh->ratio;
+  cf->coff = coff;
+  cf->D = sh->head_dim;
+  cf->H = sh->hidden;
+  cf->N = 2 * coff * sh->head_dim;
+  cf->rope = sh->rope_head_dim;
+  cf->rotate = sh->rotate ? 1 : 0;
+  cf->bs = sh->block_size;
+  cf->nblocks = sh->num_blocks;
+  cf->stride = sh->table_stride;
+  return CMP_OK;
+}
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct PrefillLayout {
+  size_t err, plan, rowflag, pooled, hadT, P, total;
+};
+PrefillLayout prefill_layout(const Cfg& cf, int T, int B, int out_rows) {
+  PrefillLayout L;
+  size_t o = 0;
+  L.err = o;      o += 256;
+  L.plan = o;     o = align256(o + (size_t)B * PL_WIDTH * 4);
+  L.rowflag = o;  o = align256(o + (size_t)out_rows * 4);
+  L.pooled = o;   o = align256(o + (size_t)out_rows * cf.D * 4);
+  L.hadT = o;     o = align256(o + (cf.rotate ? (size_t)cf.D * cf.D * 2 : 0));
+  L.P = o;        o = align256(o + (size_t)T * cf.N * 4);
+  L.total = o;
+  return L;
+}
+
+// decode split: K ranges per 32-column block so that about 256+ workgroups
+// stream the panel; each wave's share is a whole number of 8-step (128-k) runs
+int decode_ksplit(const Cfg& cf) {
+  const int cblocks = cf.N / 32;
+  const int units = cf.H / 512;             // 128-k runs per wave x 4 waves
+  int best = 1;
+  for (int ks = 1; ks <= units; ++ks) {
+    if (units % ks) continue;
+    best = ks;
+    if (cblocks * ks >= 256) break;
+  }
+  return best;
+}
+
+constexpr int kDecodeMaxBatch = 64;
+
+struct DecodeLayout {
+  size_t err, counters, partial, pooled, total;
+  int ks;
+};
+DecodeLayout decode_layout(const Cfg& cf, int B) {
+  DecodeLayout L;
+  L.ks = decode_ksplit(cf);
+  size_t o = 0;
+  L.err = o;       o += 256;
+  L.counters = o;  o = align256(o + (size_t)B * 4);
+  L.partial = o;   o = align256(o + (size_t)L.ks * B * cf.N * 4);
+  L.pooled = o;    o = align256(o + (size_t)B * cf.D * 4);
+  L.total = o;
+  return L;
+}
+
+int check_args(const Cfg& cf, const compressor_args* a, bool decode) {
+  if (!a) return CMP_ERR_NULLPTR;
+  if (a->batch < 1 || a->T < 0) return CMP_ERR_INVALID;
+  if (a->out_rows < 0) return CMP_ERR_OUT_ROWS;
+  if (a->T > 0 && !a->x) return CMP_ERR_NULLPTR;
+  if (!a->kv_state || !a->score_state || !a->state_block_table || !a->w_packed || !a->ape ||
+      !a->norm_weight || !a->out || !a->workspace)
+    return CMP_ERR_NULLPTR;
+  if (a->out_rows > 0 && (!a->sin || !a->cos)) return CMP_ERR_NULLPTR;
+  if (cf.rotate && !a->hadamard) return CMP_ERR_NULLPTR;
+  if (decode) {
+    if (a->cu_seqlens) return CMP_ERR_INVALID;
+    if (a->T != a->batch) return CMP_ERR_INVALID;
+    if (a->batch > kDecodeMaxBatch) return CMP_ERR_UNSUPPORTED;
+  } else if (!a->cu_seqlens && a->T % a->batch) {
+    return CMP_ERR_INVALID;
+  }
+  return CMP_OK;
+}
+
+// Kernels that use more than the default 64 KiB of dynamic LDS, set once per
+// process for the current device.
+int ensure_lds_limits() {
+  static std::once_flag flag;
+  static hipError_t status = hipSuccess;
+  std::call_once(flag, [] {
+    hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_proj_kernel<true>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        2 * GM_STAGE_BYTES);
+    hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(post_kernel<8>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        POST_ROWS * 512 * 2);
+    hipError_t e3 = hipFuncSetAttribute(reinterpret_cast<const void*>(post_kernel<2>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        POST_ROWS * 128 * 2);
+    status = e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3);
+  });
+  return status == hipSuccess ? CMP_OK : CMP_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* compressor_status_str(int status) {
+  switch (status) {
+    case CMP_OK: return "ok";
+    case CMP_ERR_NULLPTR: return "a required pointer is NULL";
+    case CMP_ERR_INVALID: return "shape or range violation";
+    case CMP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CMP_ERR_WORKSPACE: return "workspace too small";
+    case CMP_ERR_OUT_ROWS: return "out_rows too small";
+    case CMP_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int compressor_prefill_workspace_size(const compressor_shape* shape, int32_t T, int32_t batch,
+                                      int32_t out_rows, size_t* bytes) {
+  Cfg cf;
+  CMP_TRY(check_shape(shape, &cf));
+  if (!bytes) return CMP_ERR_NULLPTR;
+  if (T < 0 || batch < 1 || out_rows < 0) return CMP_ERR_INVALID;
+  *bytes = prefill_layout(cf, T, batch, out_rows).total;
+  return CMP_OK;
+}
+
+int compressor_decode_workspace_size(const compressor_shape* shape, int32_t batch,
+                                     int32_t out_rows, size_t* bytes) {
+  Cfg cf;
+  CMP_TRY(check_shape(shape, &cf));
+  if (!bytes) return CMP_ERR_NULLPTR;
+  if (batch < 1 || out_rows < 0) return CMP_ERR_INVALID;
+  if (batch > kDecodeMaxBatch) return CMP_ERR_UNSUPPORTED;
+  *bytes = decode_layout(cf, batch).total;
+  return CMP_OK;
+}
+
+int compressor_pack_weights(const compressor_shape* shape, const void* wkv, const void* wgate,
+                            void* w_packed, void* stream) {
+  Cfg cf;
+  CMP_TRY(check_shape(shape, &cf));
+  if (!wkv || !wgate || !w_packed) return CMP_ERR_NULLPTR;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launch("pack", st, [&] {
+    hipLaunchKernelGGL(pack_weights_kernel, dim3(cf.N), dim3(256), 0, st, cf,
+                       static_cast<const uint16_t*>(wkv), static_cast<const uint16_t*>(wgate),
+                       static_cast<uint16_t*>(w_packed));
+  });
+}
+
+int compressor_state_init(const compressor_shape* shape, float* kv_state, float* score_state,
+                          void* stream) {
+  Cfg cf;
+  CMP_TRY(check_shape(shape, &cf));
+  if (!kv_state || !score_state) return CMP_ERR_NULLPTR;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long n = (long)cf.nblocks * cf.bs * cf.coff * cf.D;
+  CMP_TRY(launch("state_fill", st, [&] {
+    hipLaunchKernelGGL(fill_kernel, dim3(1024), dim3(256), 0, st, kv_state, n, 0.f);
+  }));
+  return launch("state_fill", st, [&] {
+    hipLaunchKernelGGL(fill_kernel, dim3(1024), dim3(256), 0, st, score_state, n, -INFINITY);
+  });
+}
+
+int compressor_state_reset(const compressor_shape* shape, float* kv_state, float* score_state,
+                           const int32_t* kv_block_table, const int32_t* state_block_table,
+                           const int32_t* rows, int32_t n, void* stream) {
+  Cfg cf;
+  CMP_TRY(check_shape(shape, &cf));
+  if (n < 0) return CMP_ERR_INVALID;
+  if (n == 0) return CMP_OK;
+  if (!kv_state || !score_state || !state_block_table || !rows) return CMP_ERR_NULLPTR;
+  const int32_t* kvt = kv_block_table ? kv_block_table : state_block_table;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int used = (cf.coff * cf.ratio + cf.bs - 1) / cf.bs;
+  return launch("state_fill", st, [&] {
+    hipLaunchKernelGGL(reset_rows_kernel, dim3(used, n), dim3(256), 0, st, cf, kv_state,
+                       score_state, kvt, state_block_table, rows);
+  });
+}
+
+int compressor_prefill(const compressor_shape* shape, const compressor_args* a, void* stream) {
+  Cfg cf;
+  CMP_TRY(check_shape(shape, &cf));
+  CMP_TRY(check_args(cf, a, false));
+  const PrefillLayout L = prefill_layout(cf, a->T, a->batch, a->out_rows);
+  if (a->workspace_bytes < L.total) return CMP_ERR_WORKSPACE;
+  CMP_TRY(ensure_lds_limits());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  uint32_t* err = reinterpret_cast<uint32_t*>(ws + L.err);
+  int32_t* plan = reinterpret_cast<int32_t*>(ws + L.plan);
+  int32_t* rowflag = reinterpret_cast<int32_t*>(ws + L.rowflag);
+  float* pooled = reinterpret_cast<float*>(ws + L.pooled);
+  uint16_t* hadT = reinterpret_cast<uint16_t*>(ws + L.hadT);
+  float* P = reinterpret_cast<float*>(ws + L.P);
+  const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
+  const int B = a->batch, T = a->T;
+
+  CMP_TRY(launch("plan", st, [&] {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, a->cu_seqlens,
+                       a->seqused, a->start_pos, B, T, cf.ratio, a->out_rows, plan, err);
+  }));
+  if (cf.rotate) {
+    CMP_TRY(launch("hadamard_t", st, [&] {
+      hipLaunchKernelGGL(transpose_bf16_kernel, dim3(cf.D / 32, cf.D / 32), dim3(256), 0, st,
+                         static_cast<const uint16_t*>(a->hadamard), hadT, cf.D);
+    }));
+  }
+  if (T > 0) {
+    const int tiles_m = (T + GM_BM - 1) / GM_BM, tiles_n = cf.N / GM_BN;
+    const int tiles = tiles_m * tiles_n;
+    const int grid = (tiles + 7) / 8 * 8;
+    const int lds = 2 * GM_STAGE_BYTES;
+    CMP_TRY(launch("gemm", st, [&] {
+      hipLaunchKernelGGL(gemm_proj_kernel<true>, dim3(grid), dim3(GM_THREADS), lds, st,
+                         static_cast<const uint16_t*>(a->x),
+                         static_cast<const uint16_t*>(a->w_packed), P, T, cf.N, cf.H, tiles_m,
+                         tiles_n);
+    }));
+  }
+  if (a->out_rows > 0) {
+    const dim3 pg((a->out_rows + 3) / 4);
+    CMP_TRY(launch("pool", st, [&] {
+      if (cf.D == 512)
+        hipLaunchKernelGGL(pool_kernel<8>, pg, dim3(256), 0, st, cf, P, a->kv_state,
+                           a->score_state, kvt, a->state_block_table, a->ape, plan, B,
+                           a->out_rows, pooled, rowflag, err);
+      else
+        hipLaunchKernelGGL(pool_kernel<2>, pg, dim3(256), 0, st, cf, P, a->kv_state,
+                           a->score_state, kvt, a->state_block_table, a->ape, plan, B,
+                           a->out_rows, pooled, rowflag, err);
+    }));
+    const dim3 qg((a->out_rows + POST_ROWS - 1) / POST_ROWS);
+    const int lds = cf.rotate ? POST_ROWS * cf.D * 2 : 0;
+    CMP_TRY(launch("post", st, [&] {
+      if (cf.D == 512) {
+        hipLaunchKernelGGL(post_kernel<8>, qg, dim3(256), lds, st, cf, pooled, rowflag,
+                           a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
+                           static_cast<const uint16_t*>(a->cos),
+                           static_cast<const uint16_t*>(a->sin), hadT,
+                           static_cast<uint16_t*>(a->out));
+      } else {
+        hipLaunchKernelGGL(post_kernel<2>, qg, dim3(256), lds, st, cf, pooled, rowflag,
+                           a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
+                           static_cast<const uint16_t*>(a->cos),
+                           static_cast<const uint16_t*>(a->sin), hadT,
+                           static_cast<uint16_t*>(a->out));
+      }
+    }));
+  }
+  if (T > 0) {
+    CMP_TRY(launch("writeback", st, [&] {
+      hipLaunchKernelGGL(writeback_kernel, dim3(cf.coff * cf.ratio, B), dim3(256), 0, st, cf, P,
+                         a->kv_state, a->score_state, kvt, a->state_block_table, a->ape, plan,
+                         err);
+    }));
+  }
+  return CMP_OK;
+}
+
+int compressor_decode(const compressor_shape* shape, const compressor_args* a, void* stream) {
+  Cfg cf;
+  CMP_TRY(check_shape(shape, &cf));
+  CMP_TRY(check_args(cf, a, true));
+  const DecodeLayout L = decode_layout(cf, a->batch);
+  if (a->workspace_bytes < L.total) return CMP_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  uint32_t* err = reinterpret_cast<uint32_t*>(ws + L.err);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + L.counters);
+  float* partial = reinterpret_cast<float*>(ws + L.partial);
+  float* pooled = reinterpret_cast<float*>(ws + L.pooled);
+  const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
+  const int B = a->batch;
+  const int steps = cf.H / 16 / (L.ks * 4);
+  const dim3 gg(cf.N / 32, L.ks);
+  CMP_TRY(launch("gemv", st, [&] {
+    const uint16_t* X = static_cast<const uint16_t*>(a->x);
+    const uint16_t* W = static_cast<const uint16_t*>(a->w_packed);
+    if (B <= 32)
+      hipLaunchKernelGGL(gemv_kernel<1>, gg, dim3(GV_THREADS), 0, st, X, W, partial, B, cf.N,
+                         cf.H, steps, counters, B, err);
+    else
+      hipLaunchKernelGGL(gemv_kernel<2>, gg, dim3(GV_THREADS), 0, st, X, W, partial, B, cf.N,
+                         cf.H, steps, counters, B, err);
+  }));
+  return launch("decode_tail", st, [&] {
+    hipLaunchKernelGGL(decode_tail_kernel, dim3(B * (cf.D / 64) + 1), dim3(TL_THREADS), 0, st,
+                       cf, partial, L.ks, B, a->seqused, a->start_pos, a->ape, a->kv_state,
+                       a->score_state, kvt, a->state_block_table,
+                       static_cast<const uint16_t*>(a->norm_weight),
+                       static_cast<const uint16_t*>(a->cos), static_cast<const uint16_t*>(a->sin),
+                       static_cast<const uint16_t*>(a->hadamard), static_cast<uint16_t*>(a->out),
+                       a->out_rows, pooled, counters, err);
+  });
+}
+
+int compressor_last_device_error(const void* workspace, void* stream, int32_t* code) {
+  if (!workspace || !code) return CMP_ERR_NULLPTR;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return CMP_ERR_HIP;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return CMP_ERR_HIP;
+  *code = int32_t(v);
+  return CMP_OK;
+}
+
+int compressor_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (auto& r : g_timing.recs) g_timing.spare.push_back({r.start, r.stop});
+  g_timing.recs.clear();
+  g_timing.on = on != 0;
+  return CMP_OK;
+}
+
+int compressor_timing_query(const char* kernel, int32_t* launches, double* total_ms) {
+  if (!kernel || !launches || !total_ms) return CMP_ERR_NULLPTR;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  int n = 0;
+  double tot = 0.0;
+  for (auto& r : g_timing.recs) {
+    if (r.name != kernel) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return CMP_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return CMP_ERR_HIP;
+    tot += ms;
+    ++n;
+  }
+  *launches = n;
+  *total_ms = tot;
+  return CMP_OK;
+}
+
+}  // extern "C"

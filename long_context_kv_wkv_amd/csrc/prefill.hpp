@@ -1,0 +1,384 @@
+// Prefill kernels other than the projection GEMM: request plan, window
+// pooling, post-processing (RMSNorm, RoPE, Hadamard), state write-back.
+#pragma once
+#include "common.hpp"
+
+namespace cmp {
+
+// ---------------------------------------------------------------------------
+// Plan: per-request start / length / windows / output rows, computed on the
+// device from cu_seqlens, seqused and start_pos (no host synchronisation).
+// Also clears the error word of this call.
+//   n_b   = seqused[b] (or the slot length)        e_b = s_b + n_b
+//   c_b   = floor(e_b / r) - floor(s_b / r)        windows completed here
+//   u_b   = ceil(n_b / r)                          output rows owned
+//   o_b   = sum_{b' < b} u_b'                      first output row
+// Windows complete when (start_pos + i + 1) % ratio == 0 ([PyPTO]
+// 数值精度与验证要点), which is what c_b counts.  Rows per request and their
+// placement are the output layout documented in compressor.h.
+// One workgroup of 1024 threads; B is walked in chunks with a carried offset.
+// ---------------------------------------------------------------------------
+constexpr int PLAN_THREADS = 1024;
+
+__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ seqused,
+    const int32_t* __restrict__ start_pos, int B, int T, int ratio, int out_rows,
+    int32_t* __restrict__ plan, uint32_t* __restrict__ err) {
+  __shared__ int scan[PLAN_THREADS];
+  __shared__ uint32_t s_err;
+  __shared__ int s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) { s_err = 0; s_carry = 0; }
+  __syncthreads();
+  uint32_t my_err = 0;
+  for (int base = 0; base < B; base += PLAN_THREADS) {
+    const int b = base + tid;
+    int s = 0, n = 0, row0 = 0;
+    if (b < B) {
+      int c0, c1;
+      if (cu_seqlens) { c0 = cu_seqlens[b]; c1 = cu_seqlens[b + 1]; }
+      else { const int S = T / B; c0 = b * S; c1 = c0 + S; }
+      if (c0 < 0 || c1 < c0 || c1 > T) { my_err |= CMP_DEVERR_SEQLEN; c0 = 0; c1 = 0; }
+      const int slot = c1 - c0;
+      n = seqused ? seqused[b] : slot;
+      if (n < 0 || n > slot) { my_err |= CMP_DEVERR_SEQLEN; n = n < 0 ? 0 : slot; }
+      s = start_pos ? start_pos[b] : 0;
+      if (s < 0 || s > 0x7fffffff - n) { my_err |= CMP_DEVERR_START_POS; s = 0; n = 0; }
+      row0 = c0;
+    }
+    const int u = (n + ratio - 1) / ratio;
+    scan[tid] = u;
+    __syncthreads();
+    for (int off = 1; off < PLAN_THREADS; off <<= 1) {     // inclusive scan
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    if (b < B) {
+      const int e = s + n;
+      int32_t* rec = plan + (long)b * PL_WIDTH;
+      rec[PL_START] = s;
+      rec[PL_NTOK] = n;
+      rec[PL_END] = e;
+      rec[PL_ROW0] = row0;
+      rec[PL_NWIN] = e / ratio - s / ratio;
+      rec[PL_NROWS] = u;
+      rec[PL_OUT0] = s_carry + scan[tid] - u;
+      rec[PL_PAD] = 0;
+    }
+    __syncthreads();
+    if (tid == PLAN_THREADS - 1) s_carry += scan[tid];
+    __syncthreads();
+  }
+  if (my_err) atomicOr(&s_err, my_err);
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t e = s_err;
+    if (s_carry > out_rows) e |= CMP_DEVERR_OUT_ROWS;
+    *err = e;                                       // this call's error word
+  }
+}
+
+// Request owning output row `row` (largest b with o_b <= row), or -1.
+__device__ __forceinline__ int find_request(const int32_t* __restrict__ plan, int B, int row) {
+  int lo = 0, hi = B - 1, ans = -1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    if (plan[(long)mid * PL_WIDTH + PL_OUT0] <= row) { ans = mid; lo = mid + 1; }
+    else hi = mid - 1;
+  }
+  return ans;
+}
+
+// ---------------------------------------------------------------------------
+// Window pooling.  One wave per output row; lane l owns channels
+// [l*CPL, l*CPL + CPL).  For the k-th completed window w of request b the
+// slots are ([PyPTO] 压缩窗口与状态更新; [AscendC] C4A / C128A 计算公式):
+//   coff = 1: positions w*r + j, all D channels;
+//   coff = 2: channels [0, D) of positions (w-1)*r + j ("a" set), then
+//             channels [D, 2D) of positions w*r + j ("b" set);
+// a position of this call reads the projection (plus Ape on scores), an
+// earlier one the state ring as it was at call entry, a negative one is
+// padding (weight 0).  Softmax over slots per channel, times kv, summed
+// ([CANN] 计算公式 steps 3-5), evaluated as a running max / sum.
+// Output: pooled fp32 row and a flag (1 = row holds a window).
+// ---------------------------------------------------------------------------
+template <int CPL>
+__global__ __launch_bounds__(256) void pool_kernel(
+    Cfg cf, const float* __restrict__ P, const float* __restrict__ kv_state,
+    const float* __restrict__ score_state, const int32_t* __restrict__ kv_tab,
+    const int32_t* __restrict__ st_tab, const float* __restrict__ ape,
+    const int32_t* __restrict__ plan, int B, int out_rows, float* __restrict__ pooled,
+    int32_t* __restrict__ rowflag, uint32_t* __restrict__ err) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= out_rows) return;
+  const int b = find_request(plan, B, row);
+  const int32_t* rec = plan + (long)(b < 0 ? 0 : b) * PL_WIDTH;
+  const int k = row - rec[PL_OUT0];
+  if (b < 0 || k >= rec[PL_NWIN]) {
+    if (lane == 0) rowflag[row] = 0;
+    return;
+  }
+  const int r = cf.ratio, D = cf.D, cD = cf.coff * cf.D;
+  const int s = rec[PL_START], row0 = rec[PL_ROW0];
+  const int w = s / r + k;
+  const int c0 = lane * CPL;
+
+  float m[CPL], l[CPL], acc[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) { m[i] = -INFINITY; l[i] = 0.f; acc[i] = 0.f; }
+  uint32_t bad = 0;
+
+  const int nslots = cf.coff * r;
+  for (int j = 0; j < nslots; ++j) {
+    const int cs = (cf.coff == 2) ? (j >= r) : 0;
+    const int p = (cf.coff == 2) ? (w - 1 + cs) * r + (j - cs * r) : w * r + j;
+    if (p < 0) continue;                                  // padding: weight 0
+    float kv[CPL], z[CPL];
+    if (p >= s) {
+      const float* prow = P + (size_t)(row0 + (p - s)) * cf.N;
+      const int ck = packed_col(0, cs, c0, cf.coff), cz = packed_col(1, cs, c0, cf.coff);
+      const float* ap = ape + (long)(p % r) * cD + cs * D + c0;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) { kv[i] = prow[ck + i]; z[i] = prow[cz + i] + ap[i]; }
+    } else {
+      long rk, rs;
+      const bool okk = state_row(cf, kv_tab, b, p, &rk);
+      const bool oks = state_row(cf, st_tab, b, p, &rs);
+      if (!okk || !oks) { bad |= CMP_DEVERR_TABLE; continue; }
+      const float* kp = kv_state + rk * cD + cs * D + c0;
+      const float* sp = score_state + rs * cD + cs * D + c0;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) { kv[i] = kp[i]; z[i] = sp[i]; }
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      if (z[i] == -INFINITY) continue;
+      const float mn = fmaxf(m[i], z[i]);
+      const float sc = __expf(m[i] - mn), pe = __expf(z[i] - mn);
+      l[i] = l[i] * sc + pe;
+      acc[i] = acc[i] * sc + pe * kv[i];
+      m[i] = mn;
+    }
+  }
+  float* dst = pooled + (size_t)row * D + c0;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) dst[i] = l[i] > 0.f ? acc[i] / l[i] : 0.f;
+  if (lane == 0) rowflag[row] = 1;
+  if (bad && lane == 0) set_error(err, bad);
+}
+
+// ---------------------------------------------------------------------------
+// Post-processing of 64 pooled rows per workgroup: RMSNorm (eps 1e-6, fp32,
+// times the weight), interleaved RoPE on channels [D-64, D) ([PyPTO]
+// 压缩窗口与状态更新 / 算子级辅助函数), then either the bf16 store or, with
+// rotate, out = y @ Had as a bf16 MFMA product (K = D) against the
+// transposed matrix HadT[n][k] = Had[k][n].  Rows without a window are +0.
+// Pairs (2i, 2i+1) of the rotary slice rotate together: the even element with
+// cos/sin column i, the odd one with column 32 + i.
+// ---------------------------------------------------------------------------
+constexpr int POST_ROWS = 64;
+
+template <int CPL>
+__global__ __launch_bounds__(256) void post_kernel(
+    Cfg cf, const float* __restrict__ pooled, const int32_t* __restrict__ rowflag, int out_rows,
+    const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ cosv,
+    const uint16_t* __restrict__ sinv, const uint16_t* __restrict__ hadT,
+    uint16_t* __restrict__ out) {
+  constexpr int D = CPL * 64;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [64][D] bf16, swizzled
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row_base = blockIdx.x * POST_ROWS;
+  const int c0 = lane * CPL;
+  const int rope0 = D - cf.rope;
+  float g[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) g[i] = bf2f(gamma[c0 + i]);
+
+  for (int rr = 0; rr < POST_ROWS / 4; ++rr) {
+    const int lr = wave * (POST_ROWS / 4) + rr;
+    const int row = row_base + lr;
+    if (row >= out_rows) break;
+    float y[CPL];
+    const bool live = rowflag[row] != 0;
+    if (live) {
+      const float* src = pooled + (size_t)row * D + c0;
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) { y[i] = src[i]; ss += y[i] * y[i]; }
+      ss = wave_sum(ss);
+      const float inv = rsqrtf(ss / float(D) + kRmsEps);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) y[i] = y[i] * inv * g[i];
+      if (c0 >= rope0) {
+        const uint16_t* cr = cosv + (size_t)row * cf.rope;
+        const uint16_t* sr = sinv + (size_t)row * cf.rope;
+        const int half = cf.rope / 2;
+#pragma unroll
+        for (int i = 0; i < CPL; i += 2) {
+          const int pr = (c0 + i - rope0) >> 1;
+          const float e = y[i], o = y[i + 1];
+          y[i] = e * bf2f(cr[pr]) - o * bf2f(sr[pr]);
+          y[i + 1] = o * bf2f(cr[half + pr]) + e * bf2f(sr[half + pr]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) y[i] = 0.f;
+    }
+    if (!cf.rotate) {
+      uint16_t* dst = out + (size_t)row * D + c0;
+#pragma unroll
+      for (int i = 0; i < CPL; i += 2)
+        *reinterpret_cast<uint32_t*>(dst + i) = live ? pack_bf2(y[i], y[i + 1]) : 0u;
+    } else {
+      // LDS tile row lr: 16-byte chunk ch of the row at ((ch ^ (lr & 7)) * 16)
+#pragma unroll
+      for (int i = 0; i < CPL; i += 2) {
+        const int c = c0 + i;
+        const int ch = c >> 3, within = c & 7;
+        *reinterpret_cast<uint32_t*>(smem + lr * D * 2 + ((ch ^ (lr & 7)) << 4) + within * 2) =
+            pack_bf2(y[i], y[i + 1]);
+      }
+    }
+  }
+  if (!cf.rotate) return;
+  __syncthreads();
+
+  // out[64, D] = Y[64, D] . Had; wave w owns output columns [w*D/4, (w+1)*D/4)
+  constexpr int NB = D / 128;               // 32-column blocks per wave
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  f32x16 acc[2][NB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int nbase = wave * (D / 4);
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const int ch = kk * 2 + lhalf;
+    bf16x8 a[2], bb[NB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rr = i * 32 + lrow;
+      a[i] = *reinterpret_cast<const bf16x8*>(smem + rr * D * 2 + ((ch ^ (rr & 7)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      bb[j] = *reinterpret_cast<const bf16x8*>(hadT + (size_t)(nbase + j * 32 + lrow) * D + ch * 8);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lr = i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
+      const int row = row_base + lr;
+      if (row >= out_rows) continue;
+      const bool live = rowflag[row] != 0;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int col = nbase + j * 32 + lrow;
+        out[(size_t)row * D + col] = live ? f2bf(acc[i][j][r]) : uint16_t(0);
+      }
+    }
+}
+
+// HadT[n][k] = Had[k][n] (D x D bf16), through a 32 x 32 LDS tile.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
+                                                             uint16_t* __restrict__ outT, int D) {
+  __shared__ uint16_t tile[32][33];
+  const int bx = blockIdx.x * 32, by = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 8 rows per pass
+  for (int y = ty; y < 32; y += 8) tile[y][tx] = in[(size_t)(by + y) * D + bx + tx];
+  __syncthreads();
+  for (int y = ty; y < 32; y += 8) outT[(size_t)(bx + y) * D + by + tx] = tile[tx][y];
+}
+
+// ---------------------------------------------------------------------------
+// State write-back, after every pooling read of the call: positions
+// [max(s, r*floor(e/r) - (coff-1)*r), e) go to their ring slots, kv rows as
+// projected and score rows with Ape added ([PyPTO] 压缩窗口与状态更新: the
+// rows of an unfinished window are written to kv_state / score_state;
+// [Triton] 状态要跨调用保留).  Each position owns its slot: one writer per row.
+// One workgroup per (request, position) pair.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void writeback_kernel(
+    Cfg cf, const float* __restrict__ P, float* __restrict__ kv_state,
+    float* __restrict__ score_state, const int32_t* __restrict__ kv_tab,
+    const int32_t* __restrict__ st_tab, const float* __restrict__ ape,
+    const int32_t* __restrict__ plan, uint32_t* __restrict__ err) {
+  const int b = blockIdx.y;
+  const int32_t* rec = plan + (long)b * PL_WIDTH;
+  const int s = rec[PL_START], e = rec[PL_END], row0 = rec[PL_ROW0];
+  const int r = cf.ratio, cD = cf.coff * cf.D;
+  const int lo = max(s, r * (e / r) - (cf.coff - 1) * r);
+  const int p = lo + blockIdx.x;
+  if (p >= e) return;
+  long rk, rs;
+  const bool okk = state_row(cf, kv_tab, b, p, &rk);
+  const bool oks = state_row(cf, st_tab, b, p, &rs);
+  if (!okk || !oks) {
+    if (threadIdx.x == 0) set_error(err, CMP_DEVERR_TABLE);
+    return;
+  }
+  const float* prow = P + (size_t)(row0 + (p - s)) * cf.N;
+  const float* ap = ape + (long)(p % r) * cD;
+  for (int idx = threadIdx.x; idx < cD; idx += blockDim.x) {
+    const int cs = idx / cf.D, c = idx - cs * cf.D;
+    kv_state[rk * cD + idx] = prow[packed_col(0, cs, c, cf.coff)];
+    score_state[rs * cD + idx] = prow[packed_col(1, cs, c, cf.coff)] + ap[idx];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing and pool fills.
+// ---------------------------------------------------------------------------
+// w_packed[n] = the wkv / wgate row that column n of the panel projects.
+__global__ __launch_bounds__(256) void pack_weights_kernel(Cfg cf, const uint16_t* __restrict__ wkv,
+                                                          const uint16_t* __restrict__ wgate,
+                                                          uint16_t* __restrict__ wp) {
+  const int n = blockIdx.x;
+  const int nv = 2 * cf.coff, cpg = 128 / nv;
+  const int g = n >> 7, q = (n & 127) >> 5, i = n & 31;
+  const int v = q % nv, sub = q / nv;
+  const int c = g * cpg + sub * 32 + i;
+  const bool is_score = v >= cf.coff;
+  const int cs = is_score ? v - cf.coff : v;
+  const uint16_t* src = (is_score ? wgate : wkv) + (size_t)(cs * cf.D + c) * cf.H;
+  uint16_t* dst = wp + (size_t)n * cf.H;
+  for (int k = threadIdx.x * 8; k < cf.H; k += blockDim.x * 8)
+    *reinterpret_cast<uint4*>(dst + k) = *reinterpret_cast<const uint4*>(src + k);
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, long n, float v) {
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// Refill the ring blocks named by table rows rows[0..n): kv 0, score -inf.
+__global__ __launch_bounds__(256) void reset_rows_kernel(Cfg cf, float* __restrict__ kv_state,
+                                                        float* __restrict__ score_state,
+                                                        const int32_t* __restrict__ kv_tab,
+                                                        const int32_t* __restrict__ st_tab,
+                                                        const int32_t* __restrict__ rows) {
+  const int rb = rows[blockIdx.y];
+  const int used = (cf.coff * cf.ratio + cf.bs - 1) / cf.bs;
+  const int j = blockIdx.x;
+  if (j >= used) return;
+  const int kb = kv_tab[(long)rb * cf.stride + j], sb = st_tab[(long)rb * cf.stride + j];
+  const long blk = (long)cf.bs * cf.coff * cf.D;
+  if (kb >= 0 && kb < cf.nblocks)
+    for (long i = threadIdx.x; i < blk; i += blockDim.x) kv_state[kb * blk + i] = 0.f;
+  if (sb >= 0 && sb < cf.nblocks)
+    for (long i = threadIdx.x; i < blk; i += blockDim.x) score_state[sb * blk + i] = -INFINITY;
+}
+
+}  // namespace cmp

@@ -1,0 +1,76 @@
+"""The C-ABI library loads and exports every function include/*.h declares;
+host-only entry points and argument checks work without a GPU."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import long_context_kv_wkv_amd as cmp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names.update(re.findall(r"^(?:int|const char\*)\s+(compressor_\w+)\s*\(", src, flags=re.M))
+    return names
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == set(cmp.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cmp.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert cmp.compressor_status_str(0) == "ok"
+    assert "workspace" in cmp.compressor_status_str(4)
+    assert cmp.compressor_status_str(99) == "unknown status"
+
+
+def test_workspace_sizes_and_shape_checks():
+    sh = cmp.make_shape(4, 512, 7168, True, 128, 1, 1)
+    n = cmp.compressor_prefill_workspace_size(sh, 131072, 1, 32768)
+    # projection rows of 2048 fp32 columns dominate
+    assert n >= 131072 * 2048 * 4
+    assert cmp.compressor_decode_workspace_size(sh, 32, 32) > 0
+    for bad, status in ((cmp.make_shape(3, 512, 7168, True, 128, 1, 1), 3),
+                        (cmp.make_shape(4, 256, 7168, True, 128, 1, 1), 3),
+                        (cmp.make_shape(4, 512, 7000, True, 128, 1, 1), 2),
+                        (cmp.make_shape(4, 512, 7168, True, 2000, 1, 1), 2),
+                        (cmp.make_shape(4, 512, 7168, True, 4, 1, 1), 2),      # stride < 2
+                        (cmp.make_shape(4, 512, 7168, True, 128, 1, 1, 32), 3)):
+        with pytest.raises(cmp.CompressorError) as ei:
+            cmp.compressor_prefill_workspace_size(bad, 64, 1, 16)
+        assert ei.value.status == status
+    with pytest.raises(cmp.CompressorError) as ei:
+        cmp.compressor_decode_workspace_size(sh, 65, 65)
+    assert ei.value.status == 3
+
+
+def test_null_arguments_rejected_before_any_launch():
+    lib = cmp.library()
+    sh = cmp.make_shape(4, 512, 4096, False, 256, 8, 1)
+    assert lib.compressor_prefill(ctypes.byref(sh), None, None) == 1
+    assert lib.compressor_decode(ctypes.byref(sh), None, None) == 1
+    args = cmp.Args()                      # every pointer NULL
+    args.batch, args.T = 1, 4
+    assert lib.compressor_prefill(ctypes.byref(sh), ctypes.byref(args), None) == 1
+    assert lib.compressor_pack_weights(ctypes.byref(sh), None, None, None, None) == 1
+    assert lib.compressor_state_init(ctypes.byref(sh), None, None, None) == 1
+    assert lib.compressor_state_reset(ctypes.byref(sh), None, None, None, None, None, 0, None) == 0
+    code = ctypes.c_int32()
+    assert lib.compressor_last_device_error(None, None, ctypes.byref(code)) == 1
+    n = ctypes.c_int32()
+    ms = ctypes.c_double()
+    assert lib.compressor_timing_query(b"gemm", ctypes.byref(n), ctypes.byref(ms)) == 0
+    assert n.value == 0

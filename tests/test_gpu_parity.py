@@ -1,0 +1,293 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 oracle.
+
+Every case prints its name before it touches the GPU.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import compressor_oracle as O
+from compare import assert_out, assert_states
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def harness():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gpu_harness
+    return gpu_harness
+
+
+def _run_prefill(harness, w, rows=None, project_all=True):
+    case = harness.DeviceCase(w)
+    case.prefill()
+    torch.cuda.synchronize()
+    res = O.compressor(w, windows=rows, project_all=project_all)
+    return case, res
+
+
+SMALL = ["c4li_small", "c128a_8192", "c128a_8269", "p1_comp_128", "p1_comp_4", "p1_comp_indexer"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_prefill_config(harness, name):
+    _announce(name)
+    w = workloads.build_named(name)
+    case, res = _run_prefill(harness, w)
+    mx, mae = assert_out(case.out_bits(), res)
+    kv, sc = case.states()
+    assert_states(kv, sc, w, res)
+    assert case.device_error() == 0
+    print(f"{name}: max scaled err {mx:.2e}, MAE {mae:.2e}")
+
+
+@pytest.mark.parametrize("name", ["decode_c4a", "decode_c128a", "decode_c4a_all",
+                                  "decode_c128a_all"])
+def test_decode_config(harness, name):
+    _announce(name)
+    w = workloads.build_named(name)
+    case = harness.DeviceCase(w)
+    case.decode()
+    torch.cuda.synchronize()
+    res = O.compressor(w)
+    mx, mae = assert_out(case.out_bits(), res)
+    kv, sc = case.states()
+    assert_states(kv, sc, w, res)
+    assert case.device_error() == 0
+    nwin = int(res.plan.nwin.sum())
+    print(f"{name}: {nwin} windows, max scaled err {mx:.2e}, MAE {mae:.2e}")
+    if name.endswith("_all"):
+        assert nwin == w["batch"]
+
+
+def _varlen_small(seed_name, max_len, pad=0, rotate=True, B=8):
+    spec = dataclasses.replace(workloads.VARLEN_C4A, name=seed_name,
+                               lengths=("uniform", 1, max_len), pad_rows=pad, batch=B,
+                               rotate=rotate)
+    return workloads.build(spec, workloads.SEED_BASE + 40 + max_len + pad)
+
+
+@pytest.mark.parametrize("max_len,pad", [(700, 0), (513, 5)])
+def test_varlen_reduced(harness, max_len, pad):
+    _announce(f"varlen max_len={max_len} pad={pad}")
+    w = _varlen_small("varlen_small", max_len, pad)
+    case, res = _run_prefill(harness, w)
+    assert_out(case.out_bits(), res)
+    kv, sc = case.states()
+    assert_states(kv, sc, w, res)
+    assert case.device_error() == 0
+
+
+def test_varlen_full_sampled(harness):
+    _announce("varlen_c4a full size, sampled rows")
+    w = workloads.build_named("varlen_c4a")
+    plan = O.make_plan(4, w["batch"], w["T"], w["cu_seqlens"], w["seqused"], w["start_pos"])
+    rng = np.random.default_rng(5)
+    rows = set()
+    for b in range(w["batch"]):
+        u = int(plan.nrows[b])
+        o = int(plan.out0[b])
+        rows.update([o, o + u - 1] if u else [])
+        rows.update(int(v) for v in o + rng.integers(0, max(u, 1), 6) if u)
+    rows.update(int(v) for v in rng.integers(0, w["out_rows"], 16))
+    case, res = _run_prefill(harness, w, rows=rows, project_all=False)
+    assert_out(case.out_bits(), res, rows=rows)
+    kv, sc = case.states()
+    assert_states(kv, sc, w, res)
+    assert case.device_error() == 0
+
+
+def test_c4a_128k_sampled(harness):
+    _announce("c4a_128k full size, sampled rows")
+    w = workloads.build_named("c4a_128k")
+    rng = np.random.default_rng(6)
+    rows = {0, 1, 2, 63, 64, 32767} | set(int(v) for v in rng.integers(0, 32768, 40))
+    case, res = _run_prefill(harness, w, rows=rows, project_all=False)
+    mx, mae = assert_out(case.out_bits(), res, rows=rows)
+    kv, sc = case.states()
+    assert_states(kv, sc, w, res)
+    assert case.device_error() == 0
+    print(f"c4a_128k sampled: max scaled err {mx:.2e}, MAE {mae:.2e}")
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+def test_empty_and_zero_length_requests(harness):
+    _announce("zero-length requests")
+    w = _varlen_small("varlen_zero", 60, rotate=False, B=5)
+    # requests 1 and 3 carry no token this call
+    n = np.diff(w["cu_seqlens"]).astype(np.int64)
+    n[1] = 0
+    n[3] = 0
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    rows = np.concatenate([np.arange(w["cu_seqlens"][b], w["cu_seqlens"][b] + n[b])
+                           for b in range(5)]).astype(np.int64)
+    w = dict(w, x=w["x"][rows], T=int(cu[-1]), cu_seqlens=cu)
+    case, res = _run_prefill(harness, w)
+    assert_out(case.out_bits(), res)
+    kv, sc = case.states()
+    assert_states(kv, sc, w, res)
+
+
+def test_no_tokens_only_zero_fill(harness):
+    _announce("T == 0")
+    w = _varlen_small("varlen_t0", 10, rotate=False, B=2)
+    w = dict(w, x=np.zeros((0, w["hidden"]), np.uint16), T=0,
+             cu_seqlens=np.zeros(3, np.int32), out_rows=3,
+             cos=w["cos"][:3], sin=w["sin"][:3])
+    case = harness.DeviceCase(w)
+    case.out.fill_(1.0)
+    case.prefill()
+    torch.cuda.synchronize()
+    assert np.all(case.out_bits() == 0)
+    kv, sc = case.states()
+    assert np.array_equal(kv, w["kv_state"]) and np.array_equal(sc, w["score_state"])
+
+
+def test_block_size_one_and_trailing_rows(harness):
+    _announce("block_size 1, extra out rows")
+    spec = dataclasses.replace(workloads.VARLEN_C4A, name="bs1", block_size=1, batch=3,
+                               lengths=("uniform", 1, 90), rotate=False)
+    w = workloads.build(spec, 777)
+    w = dict(w, out_rows=w["out_rows"] + 5)
+    w["cos"], w["sin"] = workloads.rope_tables(np.arange(w["out_rows"]))
+    case, res = _run_prefill(harness, w)
+    assert_out(case.out_bits(), res)
+    kv, sc = case.states()
+    assert_states(kv, sc, w, res)
+
+
+def test_device_error_flags_without_fault(harness):
+    _announce("device error flags")
+    w = _varlen_small("varlen_err", 50, rotate=False, B=3)
+    bad = w["state_block_table"].copy()
+    bad[1, 0] = w["num_blocks"] + 7          # out of range
+    case = harness.DeviceCase(dict(w, state_block_table=bad))
+    case.prefill()
+    code = case.device_error()
+    assert code & 1, code
+    sp = w["start_pos"].copy()
+    sp[2] = -5
+    case2 = harness.DeviceCase(dict(w, start_pos=sp))
+    case2.prefill()
+    assert case2.device_error() & 2
+    # a clean call on the same workspace clears the word
+    case2.start_pos.copy_(torch.from_numpy(w["start_pos"]).to(case2.dev))
+    case2.prefill()
+    assert case2.device_error() == 0
+
+
+def test_host_side_errors(harness):
+    _announce("host-side argument errors")
+    import long_context_kv_wkv_amd as cmp
+    w = workloads.build_named("c4li_small")
+    case = harness.DeviceCase(w)
+    small = torch.empty(16, dtype=torch.uint8, device=case.dev)
+    with pytest.raises(cmp.CompressorError) as ei:
+        case.prefill(workspace=small)
+    assert ei.value.status == 4
+    with pytest.raises(cmp.CompressorError) as ei:
+        case.decode(cu_seqlens=case.cu_seqlens)
+    assert ei.value.status in (2, 3)
+
+
+# --------------------------------------------------------------------------
+# invariants on the GPU
+# --------------------------------------------------------------------------
+def test_determinism_bitwise(harness):
+    _announce("determinism")
+    w = _varlen_small("varlen_det", 400)
+    case = harness.DeviceCase(w)
+    case.prefill()
+    a = case.out_bits().copy()
+    ka, sa = case.states()
+    case.reset_state()
+    case.prefill()
+    assert np.array_equal(a, case.out_bits())
+    kb, sb = case.states()
+    assert np.array_equal(ka.view(np.uint32), kb.view(np.uint32))
+    assert np.array_equal(sa.view(np.uint32), sb.view(np.uint32))
+    wd = workloads.build_named("decode_c4a_all")
+    d = harness.DeviceCase(wd)
+    d.decode()
+    a = d.out_bits().copy()
+    d.reset_state()
+    d.decode()
+    assert np.array_equal(a, d.out_bits())
+
+
+def test_prefill_equals_token_by_token_decode(harness):
+    """Config-4 style: packed varlen prefill vs the same tokens fed one per
+    request per call through the decode entry point, state carried over."""
+    _announce("prefill vs token-by-token decode")
+    w = _varlen_small("varlen_dec", 40, rotate=True, B=6)
+    case = harness.DeviceCase(w)
+    case.prefill()
+    res = O.compressor(w)
+    full = {(b, wi): case.out_bits()[row] for b, wi, row in res.window_rows}
+    plan = res.plan
+    B, r = w["batch"], 4
+    # decode loop
+    d = harness.DeviceCase(dict(w, x=w["x"][:B], T=B, out_rows=B, cos=w["cos"][:B],
+                                sin=w["sin"][:B], seqused=None))
+    n = plan.ntok
+    got = {}
+    for t in range(int(n.max())):
+        active = (n > t).astype(np.int32)
+        rows = np.array([plan.row0[b] + min(t, max(n[b] - 1, 0)) for b in range(B)])
+        pos = (plan.start + t).astype(np.int32)
+        d.x.copy_(torch.from_numpy(w["x"][rows].view(np.int16)).to(d.dev).view(torch.bfloat16))
+        # rope rows: decode row o_b carries the prefill row of the same window
+        cos = np.zeros((B, 64), np.uint16)
+        sin = np.zeros((B, 64), np.uint16)
+        o = np.cumsum(active) - active
+        for b in range(B):
+            if active[b] and (pos[b] + 1) % r == 0:
+                k = (pos[b] + 1) // r - 1 - plan.start[b] // r
+                cos[o[b]] = w["cos"][plan.out0[b] + k]
+                sin[o[b]] = w["sin"][plan.out0[b] + k]
+        d.cos.copy_(torch.from_numpy(cos.view(np.int16)).to(d.dev).view(torch.bfloat16))
+        d.sin.copy_(torch.from_numpy(sin.view(np.int16)).to(d.dev).view(torch.bfloat16))
+        sp = torch.from_numpy(pos).to(d.dev)
+        su = torch.from_numpy(active).to(d.dev)
+        d.decode(start_pos=sp, seqused=su)
+        bits = d.out_bits()
+        for b in range(B):
+            if active[b] and (pos[b] + 1) % r == 0:
+                got[(b, (pos[b] + 1) // r - 1)] = bits[o[b]].copy()
+            elif active[b]:
+                assert np.all(bits[o[b]] == 0)
+        assert d.device_error() == 0
+    assert set(got) == set(full)
+    worst = 0.0
+    for key in full:
+        a = O.bf16_to_f64(full[key])
+        b_ = O.bf16_to_f64(got[key])
+        rms = np.sqrt(np.mean(a * a))
+        worst = max(worst, float(np.max(np.abs(a - b_) / np.maximum(np.abs(a), rms))))
+    assert worst <= 2e-2, worst
+    # live state rows agree
+    kvp, scp = case.states()
+    kvd, scd = d.states()
+    for b in range(B):
+        for p in O.live_positions(0, int(plan.end[b]), r, 2):
+            if p < 0:
+                continue
+            q = p % 8
+            kb = w["kv_block_table"][b, q // w["block_size"]]
+            sb = w["state_block_table"][b, q // w["block_size"]]
+            off = q % w["block_size"]
+            assert np.allclose(kvp[kb, off], kvd[kb, off], rtol=1e-3, atol=1e-3)
+            assert np.allclose(scp[sb, off], scd[sb, off], rtol=1e-3, atol=1e-3)

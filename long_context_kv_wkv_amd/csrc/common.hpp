@@ -42,6 +42,19 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 // 32-wide MFMA column block holds 32 consecutive channels of one variant, and
 // the 2*coff variants of a channel sit in the same lane of neighbouring blocks.
 // ---------------------------------------------------------------------------
+//
+// Memory layout of the panel (bf16): fragment-major.  Column block cb (32
+// panel columns) and k-step ks (16 values of K) form one 1 KiB fragment at
+// element offset ((cb * (K/16) + ks) * 64 + lane) * 8; lane l holds column
+// cb*32 + l%32, K values ks*16 + (l/32)*8 .. +8 - exactly the B operand of
+// one 32x32x16 MFMA.  Consecutive k-steps of a block are contiguous, so a
+// wave streaming one block reads one contiguous run of HBM.
+__host__ __device__ __forceinline__ size_t panel_offset(int col, int k, int K) {
+  const int cb = col >> 5, ks = k >> 4;
+  const int lane = (col & 31) + 32 * ((k >> 3) & 1);
+  return (((size_t)cb * (K >> 4) + ks) * 64 + lane) * 8 + (k & 7);
+}
+
 __host__ __device__ __forceinline__ int packed_col(int is_score, int cset, int c, int coff) {
   const int nv = 2 * coff;
   const int cpg = 128 / nv;                 // channels per 128-column group

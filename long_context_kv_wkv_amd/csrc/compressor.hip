@@ -128,7 +128,7 @@ int decode_ksplit(const Cfg& cf) {
 constexpr int kDecodeMaxBatch = 64;
 
 struct DecodeLayout {
-  size_t err, counters, partial, pooled, total;
+  size_t err, partial, total;
   int ks;
 };
 DecodeLayout decode_layout(const Cfg& cf, int B) {
@@ -136,9 +136,7 @@ DecodeLayout decode_layout(const Cfg& cf, int B) {
   L.ks = decode_ksplit(cf);
   size_t o = 0;
   L.err = o;       o += 256;
-  L.counters = o;  o = align256(o + (size_t)B * 4);
   L.partial = o;   o = align256(o + (size_t)L.ks * B * cf.N * 4);
-  L.pooled = o;    o = align256(o + (size_t)B * cf.D * 4);
   L.total = o;
   return L;
 }
@@ -355,9 +353,7 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + L.err);
-  int32_t* counters = reinterpret_cast<int32_t*>(ws + L.counters);
   float* partial = reinterpret_cast<float*>(ws + L.partial);
-  float* pooled = reinterpret_cast<float*>(ws + L.pooled);
   const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
   const int B = a->batch;
   const int steps = cf.H / 16 / (L.ks * 4);
@@ -367,19 +363,19 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
     const uint16_t* W = static_cast<const uint16_t*>(a->w_packed);
     if (B <= 32)
       hipLaunchKernelGGL(gemv_kernel<1>, gg, dim3(GV_THREADS), 0, st, X, W, partial, B, cf.N,
-                         cf.H, steps, counters, B, err);
+                         cf.H, steps, err);
     else
       hipLaunchKernelGGL(gemv_kernel<2>, gg, dim3(GV_THREADS), 0, st, X, W, partial, B, cf.N,
-                         cf.H, steps, counters, B, err);
+                         cf.H, steps, err);
   }));
   return launch("decode_tail", st, [&] {
-    hipLaunchKernelGGL(decode_tail_kernel, dim3(B * (cf.D / 64) + 1), dim3(TL_THREADS), 0, st,
-                       cf, partial, L.ks, B, a->seqused, a->start_pos, a->ape, a->kv_state,
-                       a->score_state, kvt, a->state_block_table,
-                       static_cast<const uint16_t*>(a->norm_weight),
+    auto tail = cf.ratio == 4 ? decode_tail_kernel<4, 2> : decode_tail_kernel<128, 1>;
+    hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, L.ks, B,
+                       a->seqused, a->start_pos, a->ape, a->kv_state, a->score_state, kvt,
+                       a->state_block_table, static_cast<const uint16_t*>(a->norm_weight),
                        static_cast<const uint16_t*>(a->cos), static_cast<const uint16_t*>(a->sin),
                        static_cast<const uint16_t*>(a->hadamard), static_cast<uint16_t*>(a->out),
-                       a->out_rows, pooled, counters, err);
+                       a->out_rows, err);
   });
 }
 

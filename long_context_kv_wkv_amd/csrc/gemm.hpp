@@ -6,8 +6,9 @@
 //
 // Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2, each wave a
 // 128 x 128 sub-tile = 4 x 4 blocks of the 32x32x16 bf16 MFMA), K step 64,
-// two LDS stages of 64 KiB.  Both operands are K-contiguous in HBM, so one
-// 16-byte load per lane feeds one MFMA operand register set.  LDS rows are
+// two LDS stages of 64 KiB.  X is read row-major (128 contiguous bytes per
+// row and K tile); the panel is fragment-major, so each 64-thread group reads
+// one contiguous 1 KiB fragment.  LDS rows are
 // 128 bytes; the 16-byte chunk index is XOR-swizzled with (row & 7) so eight
 // lanes reading eight rows hit eight distinct bank groups.
 //
@@ -43,18 +44,25 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_proj_kernel(
   const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
   const int m0 = tm * GM_BM, n0 = tn * GM_BN;
 
-  // global load assignment: chunk i of a thread is row (tid >> 3) + 32 i,
-  // 16-byte column chunk tid & 7 (the same for every i)
+  // X (row-major): chunk i of a thread is row (tid >> 3) + 32 i, 16-byte
+  // column chunk tid & 7 (the same for every i).
   const int row0 = tid >> 3, kc = tid & 7;
-  const uint16_t* gb = W + (size_t)(n0 + row0) * K + kc * 8;
   const int soff = swz(row0, kc);          // + i * 4096 for chunk i
   const int last_row = T - 1;
+  // Panel (fragment-major): chunk i of a thread is column block n0/32 + i,
+  // k-step (tid >> 6) of the 4 in the K tile, fragment lane tid & 63, i.e.
+  // panel column n0 + 32 i + (tid & 31), 16-byte K chunk 2*(tid >> 6) + ((tid >> 5) & 1).
+  const int bl = tid & 63, bks = tid >> 6;
+  const int brow = bl & 31, bkc = 2 * bks + (bl >> 5);
+  const int sboff = swz(brow, bkc);        // + i * 4096 for chunk i
+  const size_t ksteps = (size_t)(K >> 4);
+  const uint16_t* gb = W + (((size_t)(n0 >> 5) * ksteps + bks) * 64 + bl) * 8;
+  const size_t bstep = ksteps * 64 * 8;    // next column block
 
   const size_t kcol = (size_t)kc * 8;
   const uint16_t* ga[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) ga[i] = X + (size_t)min(m0 + row0 + 32 * i, last_row) * K + kcol;
-  const size_t bstep = (size_t)32 * K;
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -74,7 +82,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_proj_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     *reinterpret_cast<uint4*>(smem + soff + i * 4096) = ra[i];
-    *reinterpret_cast<uint4*>(smem + GM_BM * GM_BK * 2 + soff + i * 4096) = rb[i];
+    *reinterpret_cast<uint4*>(smem + GM_BM * GM_BK * 2 + sboff + i * 4096) = rb[i];
   }
   __syncthreads();
 
@@ -86,7 +94,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_proj_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       ra[i] = *reinterpret_cast<const uint4*>(ga[i] + k0);
-      rb[i] = *reinterpret_cast<const uint4*>(gb + i * bstep + k0);
+      rb[i] = *reinterpret_cast<const uint4*>(gb + i * bstep + (size_t)(k0 >> 4) * 512);
     }
     const uint8_t* sa = smem + (kt & 1) * GM_STAGE_BYTES;
     const uint8_t* sb = sa + GM_BM * GM_BK * 2;
@@ -110,7 +118,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_proj_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         *reinterpret_cast<uint4*>(da + soff + i * 4096) = ra[i];
-        *reinterpret_cast<uint4*>(da + GM_BM * GM_BK * 2 + soff + i * 4096) = rb[i];
+        *reinterpret_cast<uint4*>(da + GM_BM * GM_BK * 2 + sboff + i * 4096) = rb[i];
       }
     }
     __syncthreads();

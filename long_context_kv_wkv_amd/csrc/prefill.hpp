@@ -341,7 +341,9 @@ __global__ __launch_bounds__(256) void writeback_kernel(
 // ---------------------------------------------------------------------------
 // Weight packing and pool fills.
 // ---------------------------------------------------------------------------
-// w_packed[n] = the wkv / wgate row that column n of the panel projects.
+// Column n of the panel projects one wkv / wgate row (order of packed_col);
+// its K values are scattered into the fragment-major layout of panel_offset
+// in 16-byte pieces (8 consecutive K values stay together).
 __global__ __launch_bounds__(256) void pack_weights_kernel(Cfg cf, const uint16_t* __restrict__ wkv,
                                                           const uint16_t* __restrict__ wgate,
                                                           uint16_t* __restrict__ wp) {
@@ -353,9 +355,9 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(Cfg cf, const uint16_
   const bool is_score = v >= cf.coff;
   const int cs = is_score ? v - cf.coff : v;
   const uint16_t* src = (is_score ? wgate : wkv) + (size_t)(cs * cf.D + c) * cf.H;
-  uint16_t* dst = wp + (size_t)n * cf.H;
   for (int k = threadIdx.x * 8; k < cf.H; k += blockDim.x * 8)
-    *reinterpret_cast<uint4*>(dst + k) = *reinterpret_cast<const uint4*>(src + k);
+    *reinterpret_cast<uint4*>(wp + panel_offset(n, k, cf.H)) =
+        *reinterpret_cast<const uint4*>(src + k);
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, long n, float v) {

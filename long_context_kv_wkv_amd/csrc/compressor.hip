@@ -169,7 +169,7 @@ int ensure_lds_limits() {
   std::call_once(flag, [] {
     hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_proj_kernel<true>),
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        2 * GM_STAGE_BYTES);
+                                        GM_LDS_BYTES);
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(post_kernel<8>),
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         POST_ROWS * 512 * 2);
@@ -296,7 +296,7 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
     const int tiles_m = (T + GM_BM - 1) / GM_BM, tiles_n = cf.N / GM_BN;
     const int tiles = tiles_m * tiles_n;
     const int grid = (tiles + 7) / 8 * 8;
-    const int lds = 2 * GM_STAGE_BYTES;
+    const int lds = GM_LDS_BYTES;
     CMP_TRY(launch("gemm", st, [&] {
       hipLaunchKernelGGL(gemm_proj_kernel<true>, dim3(grid), dim3(GM_THREADS), lds, st,
                          static_cast<const uint16_t*>(a->x),

@@ -5,17 +5,27 @@
 // a single pass over X produces every projected column.
 //
 // Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2, each wave a
-// 128 x 128 sub-tile = 4 x 4 blocks of the 32x32x16 bf16 MFMA), K step 64,
-// two LDS stages of 64 KiB.  X is read row-major (128 contiguous bytes per
-// row and K tile); the panel is fragment-major, so each 64-thread group reads
-// one contiguous 1 KiB fragment.  LDS rows are
-// 128 bytes; the 16-byte chunk index is XOR-swizzled with (row & 7) so eight
-// lanes reading eight rows hit eight distinct bank groups.
+// 128 x 128 sub-tile = 4 x 4 blocks of the 32x32x16 bf16 MFMA, accumulators
+// in AGPRs), K step 64, two 64 KiB LDS stages filled by direct-to-LDS copies
+// (global_load_lds_dwordx4: no staging registers, no ds_write).
+//  * X tile: row-major in LDS, 128 B per row, 16-byte chunks XOR-swizzled by
+//    (row & 7) ^ ((row >> 3) & 1) so fragment reads are bank-conflict free
+//    whether LDS serves 8 or 16 lanes per cycle.  A copy instruction covers 8
+//    rows x 128 B (one cache line per row); each lane fetches the logical chunk
+//    the swizzle places at its LDS slot.
+//  * Panel tile: fragment-major like the panel in HBM (1 KiB per MFMA B
+//    fragment), copied and read lane-contiguously.
+// Per K step the 16 copies of the next tile are interleaved one per two MFMAs
+// in the first half of the step, while the second half's fragments are read;
+// the second half's MFMAs then cover the copies' latency before the single
+// wait + barrier of the step.  (Measured on MI355X: the copy stream, not the
+// MFMA rate, bounds this kernel; bursts of copies stall issue, deeper stage
+// counts lower the copy rate.)
 //
 // Workgroup order: the hardware deals workgroups round-robin to the 8 XCDs
 // (workgroup i to XCD i % 8).  Tile ids are remapped so each XCD owns a
-// contiguous run of tiles, N-fastest: the 8 N-tiles of an M-block (which
-// share that block's X rows) run together on one XCD and share its L2.
+// contiguous run of tiles, N-fastest: the N-tiles of an M-block (which share
+// that block's X rows) run together on one XCD and share its L2.
 #pragma once
 #include "common.hpp"
 
@@ -23,20 +33,30 @@ namespace cmp {
 
 constexpr int GM_BM = 256, GM_BN = 256, GM_BK = 64;
 constexpr int GM_THREADS = 256;
+constexpr int GM_STAGES = 2;
 constexpr int GM_STAGE_BYTES = (GM_BM + GM_BN) * GM_BK * 2;   // 64 KiB
+constexpr int GM_LDS_BYTES = GM_STAGES * GM_STAGE_BYTES;     // 128 KiB
 
-__device__ __forceinline__ int swz(int row, int chunk) { return (row << 7) + ((chunk ^ (row & 7)) << 4); }
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)l, 16, 0, 0);
+}
+// byte offset of 16-byte chunk `chunk` of row `row` in a 128-byte-row tile
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return (row << 7) + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+}
 
 template <bool kStoreP>
 __global__ __launch_bounds__(GM_THREADS, 1) void gemm_proj_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, float* __restrict__ P, int T,
     int N, int K, int tiles_m, int tiles_n) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // XCD-aware tile order
   const int nwg = gridDim.x;
   const int per_xcd = nwg >> 3;
   const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -44,25 +64,31 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_proj_kernel(
   const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
   const int m0 = tm * GM_BM, n0 = tn * GM_BN;
 
-  // X (row-major): chunk i of a thread is row (tid >> 3) + 32 i, 16-byte
-  // column chunk tid & 7 (the same for every i).
-  const int row0 = tid >> 3, kc = tid & 7;
-  const int soff = swz(row0, kc);          // + i * 4096 for chunk i
-  const int last_row = T - 1;
-  // Panel (fragment-major): chunk i of a thread is column block n0/32 + i,
-  // k-step (tid >> 6) of the 4 in the K tile, fragment lane tid & 63, i.e.
-  // panel column n0 + 32 i + (tid & 31), 16-byte K chunk 2*(tid >> 6) + ((tid >> 5) & 1).
-  const int bl = tid & 63, bks = tid >> 6;
-  const int brow = bl & 31, bkc = 2 * bks + (bl >> 5);
-  const int sboff = swz(brow, bkc);        // + i * 4096 for chunk i
-  const size_t ksteps = (size_t)(K >> 4);
-  const uint16_t* gb = W + (((size_t)(n0 >> 5) * ksteps + bks) * 64 + bl) * 8;
-  const size_t bstep = ksteps * 64 * 8;    // next column block
-
-  const size_t kcol = (size_t)kc * 8;
-  const uint16_t* ga[8];
+  // A copies: instruction j of wave w fills rows r0 = (8w + j) * 8 .. +8; lane l
+  // lands at LDS byte r0*128 + 16 l, i.e. row r0 + l/8, physical chunk l%8,
+  // so it fetches the logical chunk that the swizzle places there.
+  const uint16_t* asrc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ga[i] = X + (size_t)min(m0 + row0 + 32 * i, last_row) * K + kcol;
+  for (int j = 0; j < 8; ++j) {
+    const int r0 = (wave * 8 + j) * 8;
+    const int row = r0 + (lane >> 3);
+    const int kc = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
+    asrc[j] = X + (size_t)min(m0 + row, T - 1) * K + kc * 8;
+  }
+  // B copies: fragment f = 8w + j of the stage = (cb = f / 4, ks = f % 4)
+  const size_t ksteps = (size_t)(K >> 4);
+  const uint16_t* bsrc = W + ((((size_t)(n0 >> 5) + 2 * wave) * ksteps) * 64 + lane) * 8;
+
+#define ISSUE(KT_, STAGE_)                                                          \
+  {                                                                                 \
+    uint8_t* st_ = smem + (STAGE_) * GM_STAGE_BYTES;                                \
+    const int k0_ = (KT_) * GM_BK;                                                  \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                   \
+      dma16(asrc[j] + k0_, st_ + (wave * 8 + j) * 1024);                            \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                   \
+      dma16(bsrc + ((size_t)(j >> 2) * ksteps + (k0_ >> 4) + (j & 3)) * 512,        \
+            st_ + 32768 + (wave * 8 + j) * 1024);                                   \
+  }
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -72,61 +98,73 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_proj_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = K / GM_BK;
-  uint4 ra[8], rb[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ra[i] = *reinterpret_cast<const uint4*>(ga[i]);
-    rb[i] = *reinterpret_cast<const uint4*>(gb + i * bstep);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    *reinterpret_cast<uint4*>(smem + soff + i * 4096) = ra[i];
-    *reinterpret_cast<uint4*>(smem + GM_BM * GM_BK * 2 + sboff + i * 4096) = rb[i];
-  }
-  __syncthreads();
-
   const int lrow = lane & 31, lhalf = lane >> 5;
+  const int KT = K / GM_BK;
+#define WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | 0x0f70)
+#define BARRIER() asm volatile("s_barrier" ::: "memory")
+  ISSUE(0, 0);
+  WAIT_VM(0);
+  BARRIER();
   for (int kt = 0; kt < KT; ++kt) {
-    // prefetch the next K tile (the last iteration re-reads the final tile
-    // into the idle stage, which nothing reads afterwards)
-    const int k0 = min(kt + 1, KT - 1) * GM_BK;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[i] = *reinterpret_cast<const uint4*>(ga[i] + k0);
-      rb[i] = *reinterpret_cast<const uint4*>(gb + i * bstep + (size_t)(k0 >> 4) * 512);
-    }
+    const int kn = min(kt + 1, KT - 1);
+    uint8_t* stn = smem + ((kt + 1) & 1) * GM_STAGE_BYTES;
     const uint8_t* sa = smem + (kt & 1) * GM_STAGE_BYTES;
-    const uint8_t* sb = sa + GM_BM * GM_BK * 2;
+    const uint8_t* sb = sa + 32768;
+    bf16x8 a[4][4], b[4][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 a[4], b[4];
-      const int ch = kk * 2 + lhalf;
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a[i] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + i * 32 + lrow, ch));
-        b[i] = *reinterpret_cast<const bf16x8*>(sb + swz(wn * 128 + i * 32 + lrow, ch));
+        a[kk][i] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + i * 32 + lrow, kk * 2 + lhalf));
+        b[kk][i] = *reinterpret_cast<const bf16x8*>(sb + ((wn * 4 + i) * 4 + kk) * 1024 + lane * 16);
       }
+    __builtin_amdgcn_sched_barrier(0);
+    // first half: all copies of the next tile interleaved with 32 MFMAs, and
+    // the second half's fragments read from LDS
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      dma16(asrc[j] + kn * GM_BK, stn + (wave * 8 + j) * 1024);
+      dma16(bsrc + ((size_t)(j >> 2) * ksteps + (kn * GM_BK >> 4) + (j & 3)) * 512,
+            stn + 32768 + (wave * 8 + j) * 1024);
+    }
+#pragma unroll
+    for (int kk = 2; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[kk][i] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + i * 32 + lrow, kk * 2 + lhalf));
+        b[kk][i] = *reinterpret_cast<const bf16x8*>(sb + ((wn * 4 + i) * 4 + kk) * 1024 + lane * 16);
+      }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    {
-      uint8_t* da = smem + ((kt + 1) & 1) * GM_STAGE_BYTES;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][i], b[kk][j], acc[i][j], 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        *reinterpret_cast<uint4*>(da + soff + i * 4096) = ra[i];
-        *reinterpret_cast<uint4*>(da + GM_BM * GM_BK * 2 + sboff + i * 4096) = rb[i];
-      }
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 2; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][i], b[kk][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    WAIT_VM(0);
+    BARRIER();
   }
+#undef WAIT_VM
+#undef BARRIER
+#undef ISSUE
 
   if constexpr (kStoreP) {
-    // 32x32 accumulator layout: register r of lane l holds
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll

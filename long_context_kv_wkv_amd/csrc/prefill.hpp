@@ -234,12 +234,14 @@ __global__ __launch_bounds__(256) void post_kernel(
       for (int i = 0; i < CPL; i += 2)
         *reinterpret_cast<uint32_t*>(dst + i) = live ? pack_bf2(y[i], y[i + 1]) : 0u;
     } else {
-      // LDS tile row lr: 16-byte chunk ch of the row at ((ch ^ (lr & 7)) * 16)
+      // LDS tile row lr (D*2 bytes, a multiple of 256): 16-byte chunk ch at
+      // ((ch ^ (lr & 15)) * 16), so 16 consecutive rows read at one chunk
+      // index hit 16 distinct bank groups
 #pragma unroll
       for (int i = 0; i < CPL; i += 2) {
         const int c = c0 + i;
         const int ch = c >> 3, within = c & 7;
-        *reinterpret_cast<uint32_t*>(smem + lr * D * 2 + ((ch ^ (lr & 7)) << 4) + within * 2) =
+        *reinterpret_cast<uint32_t*>(smem + lr * D * 2 + ((ch ^ (lr & 15)) << 4) + within * 2) =
             pack_bf2(y[i], y[i + 1]);
       }
     }
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(256) void post_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int rr = i * 32 + lrow;
-      a[i] = *reinterpret_cast<const bf16x8*>(smem + rr * D * 2 + ((ch ^ (rr & 7)) << 4));
+      a[i] = *reinterpret_cast<const bf16x8*>(smem + rr * D * 2 + ((ch ^ (rr & 15)) << 4));
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j)

@@ -153,6 +153,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode workloads (for profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (scales HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -161,6 +163,15 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
+        return
     if a.decode_only:
         for name in ("decode_c4a", "decode_c128a", "decode_c4a_all", "decode_c128a_all"):
             print(name, json.dumps(bench_decode(name, a.decode_steps, 5)), flush=True)

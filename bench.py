@@ -68,7 +68,7 @@ def bench_prefill(steps, warmup):
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
     kernels = {}
-    for k in ("plan", "hadamard_t", "gemm", "pool", "post", "writeback"):
+    for k in ("plan", "hadamard_t", "prefix", "gemm", "post"):
         n, ms = cmp.compressor_timing_query(k)
         if n:
             kernels[k] = ms / n
@@ -182,7 +182,7 @@ def main():
     gemm_ms = pre["kernels"]["gemm"]
     flops = 2.0 * T * H * N
     achieved = flops / (gemm_ms * 1e-3) / 1e12
-    sha = kernel_source_sha("gemm.hpp", "common.hpp")
+    sha = kernel_source_sha("gemm.hpp", "pool.hpp", "common.hpp")
     traffic = load_traffic("gemm_c4a_128k_traffic.json", sha)
     result = {
         "metric": "compressed tokens/s for 128K-token C4A prefill (T=131072, H=7168, D=512, "
@@ -196,7 +196,7 @@ def main():
         "config": {"workload": "c4a_128k_prefill", "T": T, "hidden": H, "head_dim": 512,
                    "ratio": 4, "coff": 2, "rotate": True, "batch": 1, "block_size": 128,
                    "out_rows": w["out_rows"], "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "gemm_proj_kernel",
+        "roofline": {"bound": "mfma", "kernel": "gemm_pool_kernel",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": gemm_ms},

@@ -200,8 +200,9 @@ const char* compressor_status_str(int status);
 
 /* Kernel timing: while enabled, every kernel the library enqueues is
  * bracketed by a pair of HIP events on the same stream.  Enabling clears the
- * records.  Kernel names: "plan", "gemm", "pool", "post", "writeback",
- * "hadamard_t", "gemv", "decode_tail", "pack", "state_fill". */
+ * records.  Kernel names: "plan", "hadamard_t", "prefix", "gemm" (projection
+ * with the window pooling and state stores in its epilogue), "post", "gemv",
+ * "decode_tail", "pack", "state_fill". */
 int compressor_timing_enable(int32_t on);
 
 /* Wait for the recorded events, then report the number of launches of

@@ -67,7 +67,17 @@ __host__ __device__ __forceinline__ int packed_col(int is_score, int cset, int c
 // ---------------------------------------------------------------------------
 // Per-request plan record (int32 x 8) kept in the workspace.
 // ---------------------------------------------------------------------------
-enum PlanField { PL_START = 0, PL_NTOK, PL_END, PL_ROW0, PL_NWIN, PL_NROWS, PL_OUT0, PL_PAD, PL_WIDTH };
+//   START  s_b, first position of this call's tokens    NTOK  n_b
+//   END    e_b = s_b + n_b                              ROW0  packed row of s_b
+//   NWIN   windows completed in this call               NROWS ceil(n_b / r)
+//   OUT0   first output row of request b
+//   FIRST  first position the request's GEMM tiles cover (window-aligned,
+//          one window earlier for ratio 4: the halo)
+//   TILE0  index of the request's first M-tile           NTILE its M-tiles
+enum PlanField {
+  PL_START = 0, PL_NTOK, PL_END, PL_ROW0, PL_NWIN, PL_NROWS, PL_OUT0, PL_FIRST, PL_TILE0, PL_NTILE,
+  PL_WIDTH = 12
+};
 
 // Static configuration passed by value to kernels.
 struct Cfg {

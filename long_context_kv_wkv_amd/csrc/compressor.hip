@@ -12,6 +12,7 @@
 #include "common.hpp"
 #include "decode.hpp"
 #include "gemm.hpp"
+#include "pool.hpp"
 #include "prefill.hpp"
 
 using namespace cmp;
@@ -96,19 +97,28 @@ int check_shape(const compressor_shape* sh, Cfg* cf) {
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct PrefillLayout {
-  size_t err, plan, rowflag, pooled, hadT, P, total;
+  size_t err, tiles, plan, pooled, hadT, staging, split, total;
 };
+int prefill_max_tiles(const Cfg& cf, int T, int B);
 PrefillLayout prefill_layout(const Cfg& cf, int T, int B, int out_rows) {
   PrefillLayout L;
   size_t o = 0;
-  L.err = o;      o += 256;
+  L.err = 0;
+  L.tiles = 4;    o += 256;                // error word, then the GEMM tile count
   L.plan = o;     o = align256(o + (size_t)B * PL_WIDTH * 4);
-  L.rowflag = o;  o = align256(o + (size_t)out_rows * 4);
   L.pooled = o;   o = align256(o + (size_t)out_rows * cf.D * 4);
   L.hadT = o;     o = align256(o + (cf.rotate ? (size_t)cf.D * cf.D * 2 : 0));
-  L.P = o;        o = align256(o + (size_t)T * cf.N * 4);
+  L.staging = o;  o = align256(o + (size_t)B * cf.coff * cf.ratio * 2 * cf.coff * cf.D * 4);
+  L.split = o;    o = align256(o + (cf.coff == 2 ? (size_t)prefill_max_tiles(cf, T, B) * 6 * cf.D * 4 : 0));
   L.total = o;
   return L;
+}
+
+// Upper bound of the M-tiles of a call (each request adds at most two to
+// its share of T / step).
+int prefill_max_tiles(const Cfg& cf, int T, int B) {
+  (void)cf;
+  return (T + GM_BM - 1) / GM_BM + 2 * B;
 }
 
 // decode split: K ranges per 32-column block so that about 256+ workgroups
@@ -167,9 +177,13 @@ int ensure_lds_limits() {
   static std::once_flag flag;
   static hipError_t status = hipSuccess;
   std::call_once(flag, [] {
-    hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_proj_kernel<true>),
+    hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pool_kernel<4, 2>),
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         GM_LDS_BYTES);
+    hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pool_kernel<128, 1>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        GM_LDS_BYTES);
+    if (e1 == hipSuccess) e1 = e0;
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(post_kernel<8>),
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         POST_ROWS * 512 * 2);
@@ -274,17 +288,19 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + L.err);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
   int32_t* plan = reinterpret_cast<int32_t*>(ws + L.plan);
-  int32_t* rowflag = reinterpret_cast<int32_t*>(ws + L.rowflag);
   float* pooled = reinterpret_cast<float*>(ws + L.pooled);
   uint16_t* hadT = reinterpret_cast<uint16_t*>(ws + L.hadT);
-  float* P = reinterpret_cast<float*>(ws + L.P);
+  float* staging = reinterpret_cast<float*>(ws + L.staging);
+  float* split = reinterpret_cast<float*>(ws + L.split);
   const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
   const int B = a->batch, T = a->T;
 
   CMP_TRY(launch("plan", st, [&] {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, a->cu_seqlens,
-                       a->seqused, a->start_pos, B, T, cf.ratio, a->out_rows, plan, err);
+                       a->seqused, a->start_pos, B, T, cf.ratio, cf.coff, GM_BM, a->out_rows,
+                       plan, tiles, err);
   }));
   if (cf.rotate) {
     CMP_TRY(launch("hadamard_t", st, [&] {
@@ -293,52 +309,39 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
     }));
   }
   if (T > 0) {
-    const int tiles_m = (T + GM_BM - 1) / GM_BM, tiles_n = cf.N / GM_BN;
-    const int tiles = tiles_m * tiles_n;
-    const int grid = (tiles + 7) / 8 * 8;
-    const int lds = GM_LDS_BYTES;
+    CMP_TRY(launch("prefix", st, [&] {
+      hipLaunchKernelGGL(prefix_kernel, dim3(cf.coff * cf.ratio, B), dim3(256), 0, st, cf,
+                         a->kv_state, a->score_state, kvt, a->state_block_table, plan, staging,
+                         err);
+    }));
+    const int tiles_n = cf.N / GM_BN;
+    const long nwg = (long)prefill_max_tiles(cf, T, B) * tiles_n;
+    const int grid = int((nwg + 7) / 8 * 8);
     CMP_TRY(launch("gemm", st, [&] {
-      hipLaunchKernelGGL(gemm_proj_kernel<true>, dim3(grid), dim3(GM_THREADS), lds, st,
+      auto kern = cf.ratio == 4 ? gemm_pool_kernel<4, 2> : gemm_pool_kernel<128, 1>;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(GM_THREADS), GM_LDS_BYTES, st, cf,
                          static_cast<const uint16_t*>(a->x),
-                         static_cast<const uint16_t*>(a->w_packed), P, T, cf.N, cf.H, tiles_m,
-                         tiles_n);
+                         static_cast<const uint16_t*>(a->w_packed), T, B, plan, tiles, a->ape,
+                         staging, a->kv_state, a->score_state, kvt, a->state_block_table, pooled,
+                         a->out_rows, split, err);
     }));
   }
   if (a->out_rows > 0) {
-    const dim3 pg((a->out_rows + 3) / 4);
-    CMP_TRY(launch("pool", st, [&] {
-      if (cf.D == 512)
-        hipLaunchKernelGGL(pool_kernel<8>, pg, dim3(256), 0, st, cf, P, a->kv_state,
-                           a->score_state, kvt, a->state_block_table, a->ape, plan, B,
-                           a->out_rows, pooled, rowflag, err);
-      else
-        hipLaunchKernelGGL(pool_kernel<2>, pg, dim3(256), 0, st, cf, P, a->kv_state,
-                           a->score_state, kvt, a->state_block_table, a->ape, plan, B,
-                           a->out_rows, pooled, rowflag, err);
-    }));
     const dim3 qg((a->out_rows + POST_ROWS - 1) / POST_ROWS);
     const int lds = cf.rotate ? POST_ROWS * cf.D * 2 : 0;
     CMP_TRY(launch("post", st, [&] {
-      if (cf.D == 512) {
-        hipLaunchKernelGGL(post_kernel<8>, qg, dim3(256), lds, st, cf, pooled, rowflag,
+      if (cf.D == 512)
+        hipLaunchKernelGGL(post_kernel<8>, qg, dim3(256), lds, st, cf, pooled, split, plan, B,
                            a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
                            static_cast<const uint16_t*>(a->cos),
                            static_cast<const uint16_t*>(a->sin), hadT,
                            static_cast<uint16_t*>(a->out));
-      } else {
-        hipLaunchKernelGGL(post_kernel<2>, qg, dim3(256), lds, st, cf, pooled, rowflag,
+      else
+        hipLaunchKernelGGL(post_kernel<2>, qg, dim3(256), lds, st, cf, pooled, split, plan, B,
                            a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
                            static_cast<const uint16_t*>(a->cos),
                            static_cast<const uint16_t*>(a->sin), hadT,
                            static_cast<uint16_t*>(a->out));
-      }
-    }));
-  }
-  if (T > 0) {
-    CMP_TRY(launch("writeback", st, [&] {
-      hipLaunchKernelGGL(writeback_kernel, dim3(cf.coff * cf.ratio, B), dim3(256), 0, st, cf, P,
-                         a->kv_state, a->score_state, kvt, a->state_block_table, a->ape, plan,
-                         err);
     }));
   }
   return CMP_OK;

@@ -22,10 +22,9 @@
 // MFMA rate, bounds this kernel; bursts of copies stall issue, deeper stage
 // counts lower the copy rate.)
 //
-// Workgroup order: the hardware deals workgroups round-robin to the 8 XCDs
-// (workgroup i to XCD i % 8).  Tile ids are remapped so each XCD owns a
-// contiguous run of tiles, N-fastest: the N-tiles of an M-block (which share
-// that block's X rows) run together on one XCD and share its L2.
+// The tile schedule and the epilogue live in pool.hpp (the GEMM never writes
+// the projection to HBM: its epilogue pools windows straight from the
+// accumulators).
 #pragma once
 #include "common.hpp"
 
@@ -48,49 +47,34 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return (row << 7) + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
 }
 
-template <bool kStoreP>
-__global__ __launch_bounds__(GM_THREADS, 1) void gemm_proj_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, float* __restrict__ P, int T,
-    int N, int K, int tiles_m, int tiles_n) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+// ---------------------------------------------------------------------------
+// Main loop of one 256 x 256 tile: acc[i][j] (wave (wm, wn), 32x32 block i of
+// its 128 rows, block j of its 128 columns) += X[rows] . Wp[n0 .. n0+256)^T.
+// arow[j] is the packed X row that this lane's j-th copy instruction reads:
+// tile row ((wave * 8 + j) * 8 + lane / 8); rows outside the tensor must be
+// clamped by the caller to any valid row (their results are not used).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], uint8_t* smem,
+                                              const uint16_t* __restrict__ X,
+                                              const uint16_t* __restrict__ W, int K, int n0,
+                                              const int (&arow)[8]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-
-  const int nwg = gridDim.x;
-  const int per_xcd = nwg >> 3;
-  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (tile >= tiles_m * tiles_n) return;
-  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
-  const int m0 = tm * GM_BM, n0 = tn * GM_BN;
-
-  // A copies: instruction j of wave w fills rows r0 = (8w + j) * 8 .. +8; lane l
-  // lands at LDS byte r0*128 + 16 l, i.e. row r0 + l/8, physical chunk l%8,
-  // so it fetches the logical chunk that the swizzle places there.
+  // A copies: instruction j of wave w fills tile rows r0 = (8w + j) * 8 .. +8;
+  // lane l lands at LDS byte r0*128 + 16 l, i.e. row r0 + l/8, physical chunk
+  // l%8, so it fetches the logical chunk that the swizzle places there.
   const uint16_t* asrc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int r0 = (wave * 8 + j) * 8;
-    const int row = r0 + (lane >> 3);
+    const int row = (wave * 8 + j) * 8 + (lane >> 3);
     const int kc = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
-    asrc[j] = X + (size_t)min(m0 + row, T - 1) * K + kc * 8;
+    asrc[j] = X + (size_t)arow[j] * K + kc * 8;
   }
-  // B copies: fragment f = 8w + j of the stage = (cb = f / 4, ks = f % 4)
+  // B copies: fragment f = 8w + j of the stage is (column block f / 4, k-step f % 4)
   const size_t ksteps = (size_t)(K >> 4);
   const uint16_t* bsrc = W + ((((size_t)(n0 >> 5) + 2 * wave) * ksteps) * 64 + lane) * 8;
 
-#define ISSUE(KT_, STAGE_)                                                          \
-  {                                                                                 \
-    uint8_t* st_ = smem + (STAGE_) * GM_STAGE_BYTES;                                \
-    const int k0_ = (KT_) * GM_BK;                                                  \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                   \
-      dma16(asrc[j] + k0_, st_ + (wave * 8 + j) * 1024);                            \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                   \
-      dma16(bsrc + ((size_t)(j >> 2) * ksteps + (k0_ >> 4) + (j & 3)) * 512,        \
-            st_ + 32768 + (wave * 8 + j) * 1024);                                   \
-  }
-
-  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -102,10 +86,19 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_proj_kernel(
   const int KT = K / GM_BK;
 #define WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | 0x0f70)
 #define BARRIER() asm volatile("s_barrier" ::: "memory")
-  ISSUE(0, 0);
+  {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      dma16(asrc[j], smem + (wave * 8 + j) * 1024);
+      dma16(bsrc + ((size_t)(j >> 2) * ksteps + (j & 3)) * 512, smem + 32768 + (wave * 8 + j) * 1024);
+    }
+  }
   WAIT_VM(0);
   BARRIER();
   for (int kt = 0; kt < KT; ++kt) {
+    // the next tile's copies go to the other stage, which every wave finished
+    // reading before the last barrier (the last iteration re-copies tile
+    // KT-1 there; nothing reads it)
     const int kn = min(kt + 1, KT - 1);
     uint8_t* stn = smem + ((kt + 1) & 1) * GM_STAGE_BYTES;
     const uint8_t* sa = smem + (kt & 1) * GM_STAGE_BYTES;
@@ -143,10 +136,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_proj_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][i], b[kk][j], acc[i][j], 0, 0, 0);
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one copy
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -162,21 +155,6 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_proj_kernel(
   }
 #undef WAIT_VM
 #undef BARRIER
-#undef ISSUE
-
-  if constexpr (kStoreP) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 128 + j * 32 + lrow;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-          if (row < T) P[(size_t)row * N + col] = acc[i][j][r];
-        }
-      }
-  }
 }
 
 }  // namespace cmp

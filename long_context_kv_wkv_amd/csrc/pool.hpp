@@ -1,0 +1,422 @@
+// Prefill: projection GEMM with the window pooling fused into its epilogue.
+//
+// Tiles are window-aligned per request.  A tile covers 256 consecutive
+// positions P0 .. P0+255 of one request (rows of x where the position is a
+// token of this call; earlier positions come from the state ring, staged by
+// prefix_kernel before the GEMM): 64 windows for ratio 4, two for ratio 128.
+// For ratio 4 (coff = 2) window w pools the first channel set of window w-1
+// and the second set of window w ([PyPTO] 压缩窗口与状态更新; [AscendC] C4A
+// 计算公式).  The first window of a request's first tile takes window w-1 from
+// the staged state rows (or padding); in later tiles that window is split:
+// the tile stores the second-set statistics of its first window and the
+// first-set statistics of its last window, and the post kernel merges the
+// two halves of each split window (no halo recomputation, no tile waits).
+//
+// Epilogue: the accumulators of wave (wm, wn) hold 128 rows x 128 panel
+// columns; the panel's column order puts every variant (kv / score, channel
+// set) of a channel in one lane (packed_col), and a lane's rows come in runs
+// of 4 consecutive rows.  So each lane forms, per channel, the softmax
+// statistics (running max m, sum l, weighted sum x) of its window slots,
+// merges them with the statistics its neighbour lane (or, once per tile, the
+// other row-wave) holds for the rest of the window, and writes the pooled
+// value ([CANN] 计算公式 steps 3-5).  Scores get Ape first ([CANN] step 2).
+// The same epilogue stores the state rows that stay live after the call
+// (positions [max(s, r*floor(e/r) - (coff-1)*r), e)): the GEMM never reads
+// the pool, so there is no read/write hazard inside the kernel.
+#pragma once
+#include "common.hpp"
+#include "gemm.hpp"
+
+namespace cmp {
+
+// Stats (m, l, x) of softmax-weighted sums; m = -inf means empty.
+struct Soft {
+  float m, l, x;
+};
+__device__ __forceinline__ void soft_add(Soft& s, float z, float kv) {
+  const float mn = fmaxf(s.m, z);
+  const float sc = __expf(s.m - mn), pe = __expf(z - mn);
+  s.l = s.l * sc + pe;
+  s.x = s.x * sc + pe * kv;
+  s.m = mn;
+}
+__device__ __forceinline__ Soft soft_merge(Soft a, Soft b) {
+  if (a.l == 0.f) return b;
+  if (b.l == 0.f) return a;
+  const float mn = fmaxf(a.m, b.m);
+  const float sa = __expf(a.m - mn), sb = __expf(b.m - mn);
+  return Soft{mn, a.l * sa + b.l * sb, a.x * sa + b.x * sb};
+}
+__device__ __forceinline__ Soft soft_shfl_xor(Soft s, int mask) {
+  return Soft{__shfl_xor(s.m, mask, 64), __shfl_xor(s.l, mask, 64), __shfl_xor(s.x, mask, 64)};
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// For a lane of the low half, `a` of the lane 32 above; for a lane of the
+// high half, `b` of the lane 32 below (one v_permlane32_swap, no LDS).
+__device__ __forceinline__ float cross_half(float a, float b, int hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(hi ? r[0] : r[1]);
+}
+
+// Softmax statistics of one run of 4 rows (scores z, values v): the max and
+// the exp-weighted sums taken against it; an all -inf run is empty.
+__device__ __forceinline__ Soft soft_group4(const float (&z)[4], const float (&v)[4]) {
+  const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+  float l = 0.f, x = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float p = __builtin_amdgcn_exp2f((z[q] - mx) * kLog2e);
+    l += p;
+    x = fmaf(p, v[q], x);
+  }
+  return mx == -INFINITY ? Soft{-INFINITY, 0.f, 0.f} : Soft{mx, l, x};
+}
+
+// Pooled value of the union of two statistics (0 when both are empty).
+__device__ __forceinline__ float soft_value2(Soft a, Soft b) {
+  const float mn = fmaxf(a.m, b.m);
+  const float sa = a.l > 0.f ? __builtin_amdgcn_exp2f((a.m - mn) * kLog2e) : 0.f;
+  const float sb = b.l > 0.f ? __builtin_amdgcn_exp2f((b.m - mn) * kLog2e) : 0.f;
+  const float den = a.l * sa + b.l * sb;
+  return den > 0.f ? (a.x * sa + b.x * sb) / den : 0.f;
+}
+
+// Staging of the ring rows of positions [L_b, s_b) (positions >= 0): for
+// request b, row j = p - L_b holds the kv row (coff*D) then the score row.
+__global__ __launch_bounds__(256) void prefix_kernel(Cfg cf, const float* __restrict__ kv_state,
+                                                    const float* __restrict__ score_state,
+                                                    const int32_t* __restrict__ kv_tab,
+                                                    const int32_t* __restrict__ st_tab,
+                                                    const int32_t* __restrict__ plan,
+                                                    float* __restrict__ staging,
+                                                    uint32_t* __restrict__ err) {
+  const int b = blockIdx.y, j = blockIdx.x;
+  const int32_t* rec = plan + (long)b * PL_WIDTH;
+  const int p = rec[PL_FIRST] + j;
+  if (rec[PL_NTOK] == 0 || p < 0 || p >= rec[PL_START]) return;
+  const int cD = cf.coff * cf.D;
+  long rk, rs;
+  if (!state_row(cf, kv_tab, b, p, &rk) || !state_row(cf, st_tab, b, p, &rs)) {
+    if (threadIdx.x == 0) set_error(err, CMP_DEVERR_TABLE);
+    return;
+  }
+  float* dst = staging + ((size_t)b * cf.coff * cf.ratio + j) * 2 * cD;
+  for (int i = threadIdx.x; i < cD; i += blockDim.x) {
+    dst[i] = kv_state[rk * cD + i];
+    dst[cD + i] = score_state[rs * cD + i];
+  }
+}
+
+// Request whose tile range holds global M-tile `mt` (largest b with tile0 <= mt).
+__device__ __forceinline__ int find_tile_request(const int32_t* __restrict__ plan, int B, int mt) {
+  int lo = 0, hi = B - 1, ans = 0;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    if (plan[(long)mid * PL_WIDTH + PL_TILE0] <= mt) { ans = mid; lo = mid + 1; }
+    else hi = mid - 1;
+  }
+  return ans;
+}
+
+// live-state store of one position's projected row (both channel sets)
+template <int COFF>
+__device__ __forceinline__ void store_state(const Cfg& cf, float* __restrict__ kv_state,
+                                            float* __restrict__ score_state,
+                                            const int32_t* __restrict__ kv_tab,
+                                            const int32_t* __restrict__ st_tab, int b, int p,
+                                            int c, const float (&kv)[COFF], const float (&z)[COFF],
+                                            uint32_t& bad) {
+  long rk, rs;
+  if (!state_row(cf, kv_tab, b, p, &rk) || !state_row(cf, st_tab, b, p, &rs)) {
+    bad |= CMP_DEVERR_TABLE;
+    return;
+  }
+  const int cD = COFF * cf.D;
+#pragma unroll
+  for (int cs = 0; cs < COFF; ++cs) {
+    kv_state[rk * cD + cs * cf.D + c] = kv[cs];
+    score_state[rs * cD + cs * cf.D + c] = z[cs];
+  }
+}
+
+template <int R, int COFF>
+__global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
+    Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int T, int B,
+    const int32_t* __restrict__ plan, const int32_t* __restrict__ tile_count,
+    const float* __restrict__ ape, const float* __restrict__ staging,
+    float* __restrict__ kv_state, float* __restrict__ score_state,
+    const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
+    float* __restrict__ pooled, int out_rows, float* __restrict__ split,
+    uint32_t* __restrict__ err) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lrow = lane & 31, h = lane >> 5;
+  const int tiles_n = cf.N / GM_BN;
+
+  // XCD-aware order: workgroup i runs on XCD i % 8; each XCD takes a
+  // contiguous run of tiles, N fastest, so the N-tiles of an M-tile (sharing
+  // its x rows) run together and share that XCD's L2.
+  const int per_xcd = gridDim.x >> 3;
+  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int mt = tile / tiles_n, nt = tile - mt * tiles_n;
+  if (mt >= *tile_count) return;
+  const int b = find_tile_request(plan, B, mt);
+  const int32_t* rec = plan + (long)b * PL_WIDTH;
+  const int s = rec[PL_START], e = rec[PL_END], row0 = rec[PL_ROW0];
+  const int tloc = mt - rec[PL_TILE0];
+  const int P0 = R * (s / R) + tloc * GM_BM;
+  const int n0 = nt * GM_BN;
+
+  int arow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = P0 + (wave * 8 + j) * 8 + (lane >> 3);
+    arow[j] = min(max(row0 + (p - s), 0), T - 1);
+  }
+  f32x16 acc[4][4];
+  gemm_mainloop(acc, smem, X, W, cf.H, n0, arow);
+
+  const int D = cf.D, cD = COFF * D;
+  const float* stg = staging + (size_t)b * COFF * R * 2 * cD;
+  const int wfirst = s / R, wend = e / R;             // windows [wfirst, wend) complete
+  const int o = rec[PL_OUT0];
+  const int live_lo = max(s, R * (e / R) - (COFF - 1) * R);   // state rows to store
+  uint32_t bad = 0;
+
+  if constexpr (COFF == 2) {
+    // ---- ratio 4: lane (wn, lrow) owns channel c in all four variants ----
+    const int c = ((n0 + wn * 128) >> 7) * 32 + lrow;
+    float ape_a[4], ape_b[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ape_a[q] = ape[q * cD + c];
+      ape_b[q] = ape[q * cD + D + c];
+    }
+    if (tloc > 0 && P0 + GM_BM <= live_lo) {   // (live_lo <= e)
+      // Interior tile: every row is a token of this call, no state row is
+      // stored, window 0 is split and every other window is complete.  Group
+      // statistics in two passes (max, then exp) with no per-row tests.
+      Soft sa[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int i = t >> 2, r0 = 4 * (t & 3);
+        float z[4], v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          z[q] = acc[i][2][r0 + q] + ape_a[q];
+          v[q] = acc[i][0][r0 + q];
+        }
+        sa[t] = soft_group4(z, v);
+      }
+      // window 32 (first of row-wave 1) needs window 31 from row-wave 0
+      Soft* xch = reinterpret_cast<Soft*>(smem);
+      if (wm == 0 && h == 1) xch[wn * 32 + lrow] = sa[15];
+      __syncthreads();
+      const Soft from_wave0 = xch[wn * 32 + lrow];
+      float* sp = split + (size_t)mt * 6 * D;
+      if (wm == 1 && h == 1) {
+        sp[0 * D + c] = sa[15].m;
+        sp[1 * D + c] = sa[15].l;
+        sp[2 * D + c] = sa[15].x;
+      }
+      const int row_base = o + (P0 >> 2) + wm * 32 + h - wfirst;   // output row of slot 0
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int i = t >> 2, r0 = 4 * (t & 3);
+        float z[4], v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          z[q] = acc[i][3][r0 + q] + ape_b[q];
+          v[q] = acc[i][1][r0 + q];
+        }
+        const Soft sb = soft_group4(z, v);
+        // first-set statistics of window w-1: window 2t-1 (low half) sits in
+        // the high half at slot t-1, window 2t (high half) in the low half at
+        // slot t
+        const Soft& pa = sa[(t + 15) & 15];
+        Soft prev{cross_half(pa.m, sa[t].m, h), cross_half(pa.l, sa[t].l, h),
+                  cross_half(pa.x, sa[t].x, h)};
+        if (t == 0 && h == 0 && wm == 0) {
+          sp[3 * D + c] = sb.m;
+          sp[4 * D + c] = sb.l;
+          sp[5 * D + c] = sb.x;
+        } else {
+          if (t == 0 && h == 0) prev = from_wave0;
+          const int row = row_base + 2 * t;
+          if (row < out_rows) pooled[(size_t)row * D + c] = soft_value2(prev, sb);
+        }
+      }
+    } else {
+    // value of (variant, block i, register r) with prefix substitution;
+    // returns false for positions without a row (before 0, or not a token)
+    auto fetch = [&](int i, int r, int p, float (&kv)[2], float (&z)[2]) -> bool {
+      if (p >= e || p < 0) return false;
+      if (p < s) {
+        const float* row = stg + (size_t)(p - rec[PL_FIRST]) * 2 * cD;
+        kv[0] = row[c];
+        kv[1] = row[D + c];
+        z[0] = row[cD + c];
+        z[1] = row[cD + D + c];
+      } else {
+        kv[0] = acc[i][0][r];
+        kv[1] = acc[i][1][r];
+        z[0] = acc[i][2][r] + ape_a[r & 3];
+        z[1] = acc[i][3][r] + ape_b[r & 3];
+      }
+      return true;
+    };
+    // statistics of the first channel set per window this lane holds:
+    // window index in the tile w = wm*32 + 8 i + 2 i' + h, rows 4w .. 4w+3
+    Soft sa[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int ip = 0; ip < 4; ++ip) {
+        Soft st{-INFINITY, 0.f, 0.f};
+        const int w = wm * 32 + 8 * i + 2 * ip + h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float kv[2], z[2];
+          if (fetch(i, 4 * ip + q, P0 + 4 * w + q, kv, z) && z[0] != -INFINITY) soft_add(st, z[0], kv[0]);
+        }
+        sa[i][ip] = st;
+      }
+    // window 32 (first of row-wave 1) needs window 31 from row-wave 0
+    Soft* xch = reinterpret_cast<Soft*>(smem);       // [wn][32 lanes]
+    if (wm == 0 && h == 1) xch[wn * 32 + lrow] = sa[3][3];
+    __syncthreads();
+    const Soft from_wave0 = xch[wn * 32 + lrow];
+    // first-set statistics of the window before the tile: staged state rows
+    // (or padding) in the request's first tile, else the previous tile's
+    Soft before{-INFINITY, 0.f, 0.f};
+    if (tloc == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int p = P0 - 4 + q;
+        if (p >= 0) {
+          const float* row = stg + (size_t)(p - rec[PL_FIRST]) * 2 * cD;
+          const float z = row[cD + c];
+          if (z != -INFINITY) soft_add(before, z, row[c]);
+        }
+      }
+    }
+    // split-window statistics of this tile: [mt][a = last window's first
+    // set | b = first window's second set][m, l, x][D]
+    float* sp = split + (size_t)mt * 6 * D;
+    if (wm == 1 && h == 1) {
+      sp[0 * D + c] = sa[3][3].m;
+      sp[1 * D + c] = sa[3][3].l;
+      sp[2 * D + c] = sa[3][3].x;
+    }
+    // the other lane half's statistics (every lane takes part in the shuffle)
+    Soft other[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int ip = 0; ip < 4; ++ip) other[i][ip] = soft_shfl_xor(sa[i][ip], 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int ip = 0; ip < 4; ++ip) {
+        const int w = wm * 32 + 8 * i + 2 * ip + h;
+        // first-set statistics of window w-1: odd windows (h = 1) find it in
+        // the partner lane at the same slot, even ones one slot earlier
+        const Soft prev = h == 1 ? other[i][ip]
+                                 : (ip > 0 ? other[i][ip - 1]
+                                           : (i > 0 ? other[i - 1][3] : (wm == 1 ? from_wave0 : before)));
+        // second set of window w, then the pooled value
+        Soft sb{-INFINITY, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float kv[2], z[2];
+          const int p = P0 + 4 * w + q;
+          if (fetch(i, 4 * ip + q, p, kv, z)) {
+            if (z[1] != -INFINITY) soft_add(sb, z[1], kv[1]);
+            if (p >= live_lo)
+              store_state<2>(cf, kv_state, score_state, kv_tab, st_tab, b, p, c, kv, z, bad);
+          }
+        }
+        const int Wg = (P0 >> 2) + w;
+        if (Wg >= wfirst && Wg < wend) {
+          if (w == 0 && tloc > 0) {
+            sp[3 * D + c] = sb.m;
+            sp[4 * D + c] = sb.l;
+            sp[5 * D + c] = sb.x;
+          } else {
+            const Soft t = soft_merge(prev, sb);
+            const int row = o + (Wg - wfirst);
+            if (row < out_rows) pooled[(size_t)row * D + c] = t.l > 0.f ? t.x / t.l : 0.f;
+          }
+        }
+      }
+    }
+  } else {
+    // ---- ratio 128: row-wave wm holds window W0 + wm; lane (wn, lrow)
+    // owns channels c0 (blocks 0: kv, 1: score) and c1 (blocks 2, 3) ----
+    const int g = (n0 + wn * 128) >> 7;
+    const int c0 = g * 64 + lrow, c1 = c0 + 32;
+    Soft s0{-INFINITY, 0.f, 0.f}, s1{-INFINITY, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jw = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);   // row in the window
+        const int p = P0 + 128 * wm + jw;
+        float kv0 = acc[i][0][r], kv1 = acc[i][2][r];
+        float z0 = acc[i][1][r], z1 = acc[i][3][r];
+        const bool valid = p >= 0 && p < e;
+        if (valid && p < s) {
+          const float* row = stg + (size_t)(p - rec[PL_FIRST]) * 2 * cD;
+          kv0 = row[c0];
+          kv1 = row[c1];
+          z0 = row[cD + c0];
+          z1 = row[cD + c1];
+        } else if (valid) {
+          z0 += ape[jw * cD + c0];
+          z1 += ape[jw * cD + c1];
+        }
+        if (valid && z0 != -INFINITY) soft_add(s0, z0, kv0);
+        if (valid && z1 != -INFINITY) soft_add(s1, z1, kv1);
+      }
+    }
+    // state rows that stay live (only the request's last tile has any)
+    if (P0 + 128 * wm + 127 >= live_lo && P0 + 128 * wm < e) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jw = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int p = P0 + 128 * wm + jw;
+          if (p >= live_lo && p < e) {
+            long rk, rs;
+            if (state_row(cf, kv_tab, b, p, &rk) && state_row(cf, st_tab, b, p, &rs)) {
+              kv_state[rk * cD + c0] = acc[i][0][r];
+              kv_state[rk * cD + c1] = acc[i][2][r];
+              score_state[rs * cD + c0] = acc[i][1][r] + ape[jw * cD + c0];
+              score_state[rs * cD + c1] = acc[i][3][r] + ape[jw * cD + c1];
+            } else {
+              bad |= CMP_DEVERR_TABLE;
+            }
+          }
+        }
+      }
+    }
+    s0 = soft_merge(s0, soft_shfl_xor(s0, 32));
+    s1 = soft_merge(s1, soft_shfl_xor(s1, 32));
+    const int Wg = P0 / 128 + wm;
+    if (Wg >= wfirst && Wg < wend) {
+      const int row = o + (Wg - wfirst);
+      if (row < out_rows) {
+        const Soft t = h == 0 ? s0 : s1;
+        pooled[(size_t)row * D + (h == 0 ? c0 : c1)] = t.l > 0.f ? t.x / t.l : 0.f;
+      }
+    }
+  }
+  if (bad) set_error(err, bad);
+}
+
+}  // namespace cmp

@@ -22,13 +22,16 @@ constexpr int PLAN_THREADS = 1024;
 
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ seqused,
-    const int32_t* __restrict__ start_pos, int B, int T, int ratio, int out_rows,
-    int32_t* __restrict__ plan, uint32_t* __restrict__ err) {
+    const int32_t* __restrict__ start_pos, int B, int T, int ratio, int coff, int tile_rows,
+    int out_rows, int32_t* __restrict__ plan, int32_t* __restrict__ tile_count,
+    uint32_t* __restrict__ err) {
   __shared__ int scan[PLAN_THREADS];
+  __shared__ int scan2[PLAN_THREADS];
   __shared__ uint32_t s_err;
-  __shared__ int s_carry;
+  __shared__ int s_carry, s_tcarry;
   const int tid = threadIdx.x;
-  if (tid == 0) { s_err = 0; s_carry = 0; }
+  const int halo = (coff - 1) * ratio;
+  if (tid == 0) { s_err = 0; s_carry = 0; s_tcarry = 0; }
   __syncthreads();
   uint32_t my_err = 0;
   for (int base = 0; base < B; base += PLAN_THREADS) {
@@ -47,12 +50,20 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
       row0 = c0;
     }
     const int u = (n + ratio - 1) / ratio;
+    // GEMM tiles: tile_rows positions each from the window start r*floor(s/r)
+    // until e is covered; staged state rows start `halo` positions earlier
+    const int first = ratio * (s / ratio) - halo;
+    const int over = s + n - (first + halo) - tile_rows;
+    const int ntile = n == 0 ? 0 : 1 + (over > 0 ? (over + tile_rows - 1) / tile_rows : 0);
     scan[tid] = u;
+    scan2[tid] = ntile;
     __syncthreads();
-    for (int off = 1; off < PLAN_THREADS; off <<= 1) {     // inclusive scan
+    for (int off = 1; off < PLAN_THREADS; off <<= 1) {     // inclusive scans
       const int v = tid >= off ? scan[tid - off] : 0;
+      const int v2 = tid >= off ? scan2[tid - off] : 0;
       __syncthreads();
       scan[tid] += v;
+      scan2[tid] += v2;
       __syncthreads();
     }
     if (b < B) {
@@ -65,10 +76,12 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
       rec[PL_NWIN] = e / ratio - s / ratio;
       rec[PL_NROWS] = u;
       rec[PL_OUT0] = s_carry + scan[tid] - u;
-      rec[PL_PAD] = 0;
+      rec[PL_FIRST] = first;
+      rec[PL_TILE0] = s_tcarry + scan2[tid] - ntile;
+      rec[PL_NTILE] = ntile;
     }
     __syncthreads();
-    if (tid == PLAN_THREADS - 1) s_carry += scan[tid];
+    if (tid == PLAN_THREADS - 1) { s_carry += scan[tid]; s_tcarry += scan2[tid]; }
     __syncthreads();
   }
   if (my_err) atomicOr(&s_err, my_err);
@@ -77,6 +90,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     uint32_t e = s_err;
     if (s_carry > out_rows) e |= CMP_DEVERR_OUT_ROWS;
     *err = e;                                       // this call's error word
+    *tile_count = s_tcarry;
   }
 }
 
@@ -91,83 +105,13 @@ __device__ __forceinline__ int find_request(const int32_t* __restrict__ plan, in
   return ans;
 }
 
-// ---------------------------------------------------------------------------
-// Window pooling.  One wave per output row; lane l owns channels
-// [l*CPL, l*CPL + CPL).  For the k-th completed window w of request b the
-// slots are ([PyPTO] 压缩窗口与状态更新; [AscendC] C4A / C128A 计算公式):
-//   coff = 1: positions w*r + j, all D channels;
-//   coff = 2: channels [0, D) of positions (w-1)*r + j ("a" set), then
-//             channels [D, 2D) of positions w*r + j ("b" set);
-// a position of this call reads the projection (plus Ape on scores), an
-// earlier one the state ring as it was at call entry, a negative one is
-// padding (weight 0).  Softmax over slots per channel, times kv, summed
-// ([CANN] 计算公式 steps 3-5), evaluated as a running max / sum.
-// Output: pooled fp32 row and a flag (1 = row holds a window).
-// ---------------------------------------------------------------------------
-template <int CPL>
-__global__ __launch_bounds__(256) void pool_kernel(
-    Cfg cf, const float* __restrict__ P, const float* __restrict__ kv_state,
-    const float* __restrict__ score_state, const int32_t* __restrict__ kv_tab,
-    const int32_t* __restrict__ st_tab, const float* __restrict__ ape,
-    const int32_t* __restrict__ plan, int B, int out_rows, float* __restrict__ pooled,
-    int32_t* __restrict__ rowflag, uint32_t* __restrict__ err) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= out_rows) return;
+// Does output row `row` hold a window?  (Request b's k-th completed window
+// is row o_b + k; every other row is +0.)
+__device__ __forceinline__ bool row_has_window(const int32_t* __restrict__ plan, int B, int row) {
   const int b = find_request(plan, B, row);
-  const int32_t* rec = plan + (long)(b < 0 ? 0 : b) * PL_WIDTH;
-  const int k = row - rec[PL_OUT0];
-  if (b < 0 || k >= rec[PL_NWIN]) {
-    if (lane == 0) rowflag[row] = 0;
-    return;
-  }
-  const int r = cf.ratio, D = cf.D, cD = cf.coff * cf.D;
-  const int s = rec[PL_START], row0 = rec[PL_ROW0];
-  const int w = s / r + k;
-  const int c0 = lane * CPL;
-
-  float m[CPL], l[CPL], acc[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) { m[i] = -INFINITY; l[i] = 0.f; acc[i] = 0.f; }
-  uint32_t bad = 0;
-
-  const int nslots = cf.coff * r;
-  for (int j = 0; j < nslots; ++j) {
-    const int cs = (cf.coff == 2) ? (j >= r) : 0;
-    const int p = (cf.coff == 2) ? (w - 1 + cs) * r + (j - cs * r) : w * r + j;
-    if (p < 0) continue;                                  // padding: weight 0
-    float kv[CPL], z[CPL];
-    if (p >= s) {
-      const float* prow = P + (size_t)(row0 + (p - s)) * cf.N;
-      const int ck = packed_col(0, cs, c0, cf.coff), cz = packed_col(1, cs, c0, cf.coff);
-      const float* ap = ape + (long)(p % r) * cD + cs * D + c0;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) { kv[i] = prow[ck + i]; z[i] = prow[cz + i] + ap[i]; }
-    } else {
-      long rk, rs;
-      const bool okk = state_row(cf, kv_tab, b, p, &rk);
-      const bool oks = state_row(cf, st_tab, b, p, &rs);
-      if (!okk || !oks) { bad |= CMP_DEVERR_TABLE; continue; }
-      const float* kp = kv_state + rk * cD + cs * D + c0;
-      const float* sp = score_state + rs * cD + cs * D + c0;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) { kv[i] = kp[i]; z[i] = sp[i]; }
-    }
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      if (z[i] == -INFINITY) continue;
-      const float mn = fmaxf(m[i], z[i]);
-      const float sc = __expf(m[i] - mn), pe = __expf(z[i] - mn);
-      l[i] = l[i] * sc + pe;
-      acc[i] = acc[i] * sc + pe * kv[i];
-      m[i] = mn;
-    }
-  }
-  float* dst = pooled + (size_t)row * D + c0;
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) dst[i] = l[i] > 0.f ? acc[i] / l[i] : 0.f;
-  if (lane == 0) rowflag[row] = 1;
-  if (bad && lane == 0) set_error(err, bad);
+  if (b < 0) return false;
+  const int32_t* rec = plan + (long)b * PL_WIDTH;
+  return row - rec[PL_OUT0] < rec[PL_NWIN];
 }
 
 // ---------------------------------------------------------------------------
@@ -183,7 +127,8 @@ constexpr int POST_ROWS = 64;
 
 template <int CPL>
 __global__ __launch_bounds__(256) void post_kernel(
-    Cfg cf, const float* __restrict__ pooled, const int32_t* __restrict__ rowflag, int out_rows,
+    Cfg cf, const float* __restrict__ pooled, const float* __restrict__ split,
+    const int32_t* __restrict__ plan, int B, int out_rows,
     const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ cosv,
     const uint16_t* __restrict__ sinv, const uint16_t* __restrict__ hadT,
     uint16_t* __restrict__ out) {
@@ -202,12 +147,35 @@ __global__ __launch_bounds__(256) void post_kernel(
     const int row = row_base + lr;
     if (row >= out_rows) break;
     float y[CPL];
-    const bool live = rowflag[row] != 0;
+    const int rb = find_request(plan, B, row);
+    const int32_t* rrec = plan + (long)(rb < 0 ? 0 : rb) * PL_WIDTH;
+    const int k = row - rrec[PL_OUT0];
+    const bool live = rb >= 0 && k < rrec[PL_NWIN];
     if (live) {
-      const float* src = pooled + (size_t)row * D + c0;
       float ss = 0.f;
+      if (cf.coff == 2 && k > 0 && (k & 63) == 0) {
+        // a window split between two GEMM tiles: first channel set from the
+        // previous tile, second set from this one
+        const int mt = rrec[PL_TILE0] + (k >> 6);
+        const float* pa = split + (size_t)(mt - 1) * 6 * D + c0;
+        const float* pb = split + (size_t)mt * 6 * D + 3 * D + c0;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) { y[i] = src[i]; ss += y[i] * y[i]; }
+        for (int i = 0; i < CPL; ++i) {
+          float ma = pa[i], la = pa[D + i], xa = pa[2 * D + i];
+          float mb = pb[i], lb = pb[D + i], xb = pb[2 * D + i];
+          if (la == 0.f) { ma = mb; }
+          if (lb == 0.f) { mb = ma; }
+          const float mn = fmaxf(ma, mb);
+          const float sa = la == 0.f ? 0.f : __expf(ma - mn), sb = lb == 0.f ? 0.f : __expf(mb - mn);
+          const float l = la * sa + lb * sb;
+          y[i] = l > 0.f ? (xa * sa + xb * sb) / l : 0.f;
+          ss += y[i] * y[i];
+        }
+      } else {
+        const float* src = pooled + (size_t)row * D + c0;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) { y[i] = src[i]; ss += y[i] * y[i]; }
+      }
       ss = wave_sum(ss);
       const float inv = rsqrtf(ss / float(D) + kRmsEps);
 #pragma unroll
@@ -284,7 +252,7 @@ __global__ __launch_bounds__(256) void post_kernel(
       const int lr = i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
       const int row = row_base + lr;
       if (row >= out_rows) continue;
-      const bool live = rowflag[row] != 0;
+      const bool live = row_has_window(plan, B, row);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int col = nbase + j * 32 + lrow;
@@ -302,42 +270,6 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   for (int y = ty; y < 32; y += 8) tile[y][tx] = in[(size_t)(by + y) * D + bx + tx];
   __syncthreads();
   for (int y = ty; y < 32; y += 8) outT[(size_t)(bx + y) * D + by + tx] = tile[tx][y];
-}
-
-// ---------------------------------------------------------------------------
-// State write-back, after every pooling read of the call: positions
-// [max(s, r*floor(e/r) - (coff-1)*r), e) go to their ring slots, kv rows as
-// projected and score rows with Ape added ([PyPTO] 压缩窗口与状态更新: the
-// rows of an unfinished window are written to kv_state / score_state;
-// [Triton] 状态要跨调用保留).  Each position owns its slot: one writer per row.
-// One workgroup per (request, position) pair.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void writeback_kernel(
-    Cfg cf, const float* __restrict__ P, float* __restrict__ kv_state,
-    float* __restrict__ score_state, const int32_t* __restrict__ kv_tab,
-    const int32_t* __restrict__ st_tab, const float* __restrict__ ape,
-    const int32_t* __restrict__ plan, uint32_t* __restrict__ err) {
-  const int b = blockIdx.y;
-  const int32_t* rec = plan + (long)b * PL_WIDTH;
-  const int s = rec[PL_START], e = rec[PL_END], row0 = rec[PL_ROW0];
-  const int r = cf.ratio, cD = cf.coff * cf.D;
-  const int lo = max(s, r * (e / r) - (cf.coff - 1) * r);
-  const int p = lo + blockIdx.x;
-  if (p >= e) return;
-  long rk, rs;
-  const bool okk = state_row(cf, kv_tab, b, p, &rk);
-  const bool oks = state_row(cf, st_tab, b, p, &rs);
-  if (!okk || !oks) {
-    if (threadIdx.x == 0) set_error(err, CMP_DEVERR_TABLE);
-    return;
-  }
-  const float* prow = P + (size_t)(row0 + (p - s)) * cf.N;
-  const float* ap = ape + (long)(p % r) * cD;
-  for (int idx = threadIdx.x; idx < cD; idx += blockDim.x) {
-    const int cs = idx / cf.D, c = idx - cs * cf.D;
-    kv_state[rk * cD + idx] = prow[packed_col(0, cs, c, cf.coff)];
-    score_state[rs * cD + idx] = prow[packed_col(1, cs, c, cf.coff)] + ap[idx];
-  }
 }
 
 // ---------------------------------------------------------------------------

@@ -200,7 +200,7 @@ const char* compressor_status_str(int status);
 
 /* Kernel timing: while enabled, every kernel the library enqueues is
  * bracketed by a pair of HIP events on the same stream.  Enabling clears the
- * records.  Kernel names: "plan", "hadamard_t", "prefix", "gemm" (projection
+ * records.  Kernel names: "plan", "hadamard_pack", "prefix", "gemm" (projection
  * with the window pooling and state stores in its epilogue), "post", "gemv",
  * "decode_tail", "pack", "state_fill". */
 int compressor_timing_enable(int32_t on);

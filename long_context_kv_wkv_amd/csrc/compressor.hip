@@ -97,7 +97,7 @@ int check_shape(const compressor_shape* sh, Cfg* cf) {
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct PrefillLayout {
-  size_t err, tiles, plan, pooled, hadT, staging, split, total;
+  size_t err, tiles, plan, pooled, hadF, staging, split, total;
 };
 int prefill_max_tiles(const Cfg& cf, int T, int B);
 PrefillLayout prefill_layout(const Cfg& cf, int T, int B, int out_rows) {
@@ -107,7 +107,7 @@ PrefillLayout prefill_layout(const Cfg& cf, int T, int B, int out_rows) {
   L.tiles = 4;    o += 256;                // error word, then the GEMM tile count
   L.plan = o;     o = align256(o + (size_t)B * PL_WIDTH * 4);
   L.pooled = o;   o = align256(o + (size_t)out_rows * cf.D * 4);
-  L.hadT = o;     o = align256(o + (cf.rotate ? (size_t)cf.D * cf.D * 2 : 0));
+  L.hadF = o;     o = align256(o + (cf.rotate ? (size_t)cf.D * cf.D * 2 : 0));
   L.staging = o;  o = align256(o + (size_t)B * cf.coff * cf.ratio * 2 * cf.coff * cf.D * 4);
   L.split = o;    o = align256(o + (cf.coff == 2 ? (size_t)prefill_max_tiles(cf, T, B) * 6 * cf.D * 4 : 0));
   L.total = o;
@@ -291,7 +291,7 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
   int32_t* plan = reinterpret_cast<int32_t*>(ws + L.plan);
   float* pooled = reinterpret_cast<float*>(ws + L.pooled);
-  uint16_t* hadT = reinterpret_cast<uint16_t*>(ws + L.hadT);
+  uint16_t* hadF = reinterpret_cast<uint16_t*>(ws + L.hadF);
   float* staging = reinterpret_cast<float*>(ws + L.staging);
   float* split = reinterpret_cast<float*>(ws + L.split);
   const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
@@ -303,9 +303,9 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
                        plan, tiles, err);
   }));
   if (cf.rotate) {
-    CMP_TRY(launch("hadamard_t", st, [&] {
-      hipLaunchKernelGGL(transpose_bf16_kernel, dim3(cf.D / 32, cf.D / 32), dim3(256), 0, st,
-                         static_cast<const uint16_t*>(a->hadamard), hadT, cf.D);
+    CMP_TRY(launch("hadamard_pack", st, [&] {
+      hipLaunchKernelGGL(hadamard_pack_kernel, dim3(cf.D * cf.D / 8 / 256), dim3(256), 0, st,
+                         static_cast<const uint16_t*>(a->hadamard), hadF, cf.D);
     }));
   }
   if (T > 0) {
@@ -334,13 +334,13 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
         hipLaunchKernelGGL(post_kernel<8>, qg, dim3(256), lds, st, cf, pooled, split, plan, B,
                            a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
                            static_cast<const uint16_t*>(a->cos),
-                           static_cast<const uint16_t*>(a->sin), hadT,
+                           static_cast<const uint16_t*>(a->sin), hadF,
                            static_cast<uint16_t*>(a->out));
       else
         hipLaunchKernelGGL(post_kernel<2>, qg, dim3(256), lds, st, cf, pooled, split, plan, B,
                            a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
                            static_cast<const uint16_t*>(a->cos),
-                           static_cast<const uint16_t*>(a->sin), hadT,
+                           static_cast<const uint16_t*>(a->sin), hadF,
                            static_cast<uint16_t*>(a->out));
     }));
   }

@@ -115,45 +115,91 @@ __device__ __forceinline__ bool row_has_window(const int32_t* __restrict__ plan,
 }
 
 // ---------------------------------------------------------------------------
-// Post-processing of 64 pooled rows per workgroup: RMSNorm (eps 1e-6, fp32,
+// Post-processing of 64 output rows per workgroup: RMSNorm (eps 1e-6, fp32,
 // times the weight), interleaved RoPE on channels [D-64, D) ([PyPTO]
 // 压缩窗口与状态更新 / 算子级辅助函数), then either the bf16 store or, with
-// rotate, out = y @ Had as a bf16 MFMA product (K = D) against the
-// transposed matrix HadT[n][k] = Had[k][n].  Rows without a window are +0.
+// rotate, out = y @ Had as a bf16 MFMA product (K = D) against the matrix in
+// fragment-major order (hadamard_pack_kernel).  Rows without a window are +0.
 // Pairs (2i, 2i+1) of the rotary slice rotate together: the even element with
 // cos/sin column i, the odd one with column 32 + i.
+//
+// Each wave normalises 16 rows in four batches of 4 (all loads of a batch in
+// flight before the first reduction).  The product reads each Had fragment
+// once per workgroup, four k-steps ahead of its use; the result goes back
+// through the LDS tile so that the bf16 rows leave as 16-byte stores.
 // ---------------------------------------------------------------------------
 constexpr int POST_ROWS = 64;
+constexpr int POST_BATCH = 4;
+
+// N consecutive bf16 rotary columns, loaded as one piece
+template <int N>
+struct __attribute__((aligned(2 * N))) RopeCols {
+  uint16_t v[N];
+};
+
+// LDS byte offset of the 16-byte chunk `ch` of tile row `lr` (rows of D bf16,
+// D * 2 a multiple of 256): 16 consecutive rows at one chunk index hit 16
+// distinct bank groups
+template <int D>
+__device__ __forceinline__ int post_lds(int lr, int ch) {
+  return lr * D * 2 + ((ch ^ (lr & 15)) << 4);
+}
 
 template <int CPL>
 __global__ __launch_bounds__(256) void post_kernel(
     Cfg cf, const float* __restrict__ pooled, const float* __restrict__ split,
     const int32_t* __restrict__ plan, int B, int out_rows,
     const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ cosv,
-    const uint16_t* __restrict__ sinv, const uint16_t* __restrict__ hadT,
+    const uint16_t* __restrict__ sinv, const uint16_t* __restrict__ hadF,
     uint16_t* __restrict__ out) {
   constexpr int D = CPL * 64;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [64][D] bf16, swizzled
+  __shared__ int32_t row_live[POST_ROWS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row_base = blockIdx.x * POST_ROWS;
   const int c0 = lane * CPL;
-  const int rope0 = D - cf.rope;
+  const int rope0 = D - cf.rope, half = cf.rope / 2;
+  const bool rope_lane = c0 >= rope0;
+  const int pr0 = rope_lane ? (c0 - rope0) >> 1 : 0;
   float g[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) g[i] = bf2f(gamma[c0 + i]);
 
-  for (int rr = 0; rr < POST_ROWS / 4; ++rr) {
-    const int lr = wave * (POST_ROWS / 4) + rr;
-    const int row = row_base + lr;
-    if (row >= out_rows) break;
-    float y[CPL];
-    const int rb = find_request(plan, B, row);
-    const int32_t* rrec = plan + (long)(rb < 0 ? 0 : rb) * PL_WIDTH;
-    const int k = row - rrec[PL_OUT0];
-    const bool live = rb >= 0 && k < rrec[PL_NWIN];
-    if (live) {
-      float ss = 0.f;
-      if (cf.coff == 2 && k > 0 && (k & 63) == 0) {
+#pragma unroll 1
+  for (int bt = 0; bt < POST_ROWS / 4 / POST_BATCH; ++bt) {
+    const int lr0 = wave * (POST_ROWS / 4) + bt * POST_BATCH;
+    // loads of the whole batch first (rows clamped into the buffers);
+    // rope lanes also take cos/sin columns pr (even element) and half + pr
+    // (odd element) of their pairs
+    // (CPL / 2 consecutive bf16 columns per load: [0] cos pr, [1] cos half+pr,
+    // [2] sin pr, [3] sin half+pr)
+    float y[POST_BATCH][CPL];
+    RopeCols<CPL / 2> rt[POST_BATCH][4];
+#pragma unroll
+    for (int q = 0; q < POST_BATCH; ++q) {
+      const int rr = min(row_base + lr0 + q, out_rows - 1);
+      const float* src = pooled + (size_t)rr * D + c0;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) y[q][i] = src[i];
+      if (rope_lane) {
+        const uint16_t* cr = cosv + (size_t)rr * cf.rope + pr0;
+        const uint16_t* sr = sinv + (size_t)rr * cf.rope + pr0;
+        rt[q][0] = *reinterpret_cast<const RopeCols<CPL / 2>*>(cr);
+        rt[q][1] = *reinterpret_cast<const RopeCols<CPL / 2>*>(cr + half);
+        rt[q][2] = *reinterpret_cast<const RopeCols<CPL / 2>*>(sr);
+        rt[q][3] = *reinterpret_cast<const RopeCols<CPL / 2>*>(sr + half);
+      }
+    }
+    bool live[POST_BATCH];
+    float ss[POST_BATCH];
+#pragma unroll
+    for (int q = 0; q < POST_BATCH; ++q) {
+      const int row = row_base + lr0 + q;
+      const int rb = row < out_rows ? find_request(plan, B, row) : -1;
+      const int32_t* rrec = plan + (long)(rb < 0 ? 0 : rb) * PL_WIDTH;
+      const int k = row - rrec[PL_OUT0];
+      live[q] = rb >= 0 && k < rrec[PL_NWIN];
+      if (live[q] && cf.coff == 2 && k > 0 && (k & 63) == 0) {
         // a window split between two GEMM tiles: first channel set from the
         // previous tile, second set from this one
         const int mt = rrec[PL_TILE0] + (k >> 6);
@@ -168,49 +214,50 @@ __global__ __launch_bounds__(256) void post_kernel(
           const float mn = fmaxf(ma, mb);
           const float sa = la == 0.f ? 0.f : __expf(ma - mn), sb = lb == 0.f ? 0.f : __expf(mb - mn);
           const float l = la * sa + lb * sb;
-          y[i] = l > 0.f ? (xa * sa + xb * sb) / l : 0.f;
-          ss += y[i] * y[i];
+          y[q][i] = l > 0.f ? (xa * sa + xb * sb) / l : 0.f;
         }
-      } else {
-        const float* src = pooled + (size_t)row * D + c0;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) { y[i] = src[i]; ss += y[i] * y[i]; }
       }
-      ss = wave_sum(ss);
-      const float inv = rsqrtf(ss / float(D) + kRmsEps);
+      float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) y[i] = y[i] * inv * g[i];
-      if (c0 >= rope0) {
-        const uint16_t* cr = cosv + (size_t)row * cf.rope;
-        const uint16_t* sr = sinv + (size_t)row * cf.rope;
-        const int half = cf.rope / 2;
+      for (int i = 0; i < CPL; ++i) {
+        if (!live[q]) y[q][i] = 0.f;
+        acc += y[q][i] * y[q][i];
+      }
+      ss[q] = acc;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int q = 0; q < POST_BATCH; ++q) ss[q] += __shfl_xor(ss[q], off, 64);
+#pragma unroll
+    for (int q = 0; q < POST_BATCH; ++q) {
+      const int lr = lr0 + q;
+      const float inv = rsqrtf(ss[q] / float(D) + kRmsEps);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) y[q][i] = y[q][i] * inv * g[i];
+      if (rope_lane) {
 #pragma unroll
         for (int i = 0; i < CPL; i += 2) {
-          const int pr = (c0 + i - rope0) >> 1;
-          const float e = y[i], o = y[i + 1];
-          y[i] = e * bf2f(cr[pr]) - o * bf2f(sr[pr]);
-          y[i + 1] = o * bf2f(cr[half + pr]) + e * bf2f(sr[half + pr]);
+          const float e = y[q][i], o = y[q][i + 1];
+          y[q][i] = e * bf2f(rt[q][0].v[i / 2]) - o * bf2f(rt[q][2].v[i / 2]);
+          y[q][i + 1] = o * bf2f(rt[q][1].v[i / 2]) + e * bf2f(rt[q][3].v[i / 2]);
         }
       }
-    } else {
+      uint32_t pk[CPL / 2];
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) y[i] = 0.f;
-    }
-    if (!cf.rotate) {
-      uint16_t* dst = out + (size_t)row * D + c0;
-#pragma unroll
-      for (int i = 0; i < CPL; i += 2)
-        *reinterpret_cast<uint32_t*>(dst + i) = live ? pack_bf2(y[i], y[i + 1]) : 0u;
-    } else {
-      // LDS tile row lr (D*2 bytes, a multiple of 256): 16-byte chunk ch at
-      // ((ch ^ (lr & 15)) * 16), so 16 consecutive rows read at one chunk
-      // index hit 16 distinct bank groups
-#pragma unroll
-      for (int i = 0; i < CPL; i += 2) {
-        const int c = c0 + i;
-        const int ch = c >> 3, within = c & 7;
-        *reinterpret_cast<uint32_t*>(smem + lr * D * 2 + ((ch ^ (lr & 15)) << 4) + within * 2) =
-            pack_bf2(y[i], y[i + 1]);
+      for (int i = 0; i < CPL; i += 2) pk[i / 2] = live[q] ? pack_bf2(y[q][i], y[q][i + 1]) : 0u;
+      if (cf.rotate) {
+        if constexpr (CPL == 8)
+          *reinterpret_cast<uint4*>(smem + post_lds<D>(lr, lane)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        else
+          *reinterpret_cast<uint32_t*>(smem + post_lds<D>(lr, lane >> 2) + (lane & 3) * 4) = pk[0];
+        if (lane == 0) row_live[lr] = live[q];
+      } else if (row_base + lr < out_rows) {
+        uint16_t* dst = out + (size_t)(row_base + lr) * D + c0;
+        if constexpr (CPL == 8)
+          *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        else
+          *reinterpret_cast<uint32_t*>(dst) = pk[0];
       }
     }
   }
@@ -219,7 +266,11 @@ __global__ __launch_bounds__(256) void post_kernel(
 
   // out[64, D] = Y[64, D] . Had; wave w owns output columns [w*D/4, (w+1)*D/4)
   constexpr int NB = D / 128;               // 32-column blocks per wave
+  constexpr int KS = D / 16;                // k-steps
+  constexpr int PF = KS < 4 ? KS : 4;       // k-steps of Had fragments in flight
   const int lrow = lane & 31, lhalf = lane >> 5;
+  const int cb0 = wave * NB;
+  const uint16_t* hsrc = hadF + ((size_t)cb0 * KS * 64 + lane) * 8;   // fragment (cb0, 0)
   f32x16 acc[2][NB];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -227,49 +278,74 @@ __global__ __launch_bounds__(256) void post_kernel(
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int nbase = wave * (D / 4);
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const int ch = kk * 2 + lhalf;
-    bf16x8 a[2], bb[NB];
+  bf16x8 bq[PF][NB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rr = i * 32 + lrow;
-      a[i] = *reinterpret_cast<const bf16x8*>(smem + rr * D * 2 + ((ch ^ (rr & 15)) << 4));
-    }
+  for (int p = 0; p < PF; ++p)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      bb[j] = *reinterpret_cast<const bf16x8*>(hadT + (size_t)(nbase + j * 32 + lrow) * D + ch * 8);
+      bq[p][j] = *reinterpret_cast<const bf16x8*>(hsrc + ((size_t)j * KS + p) * 512);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const int ch = kk * 2 + lhalf;
+    bf16x8 a[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(smem + post_lds<D>(i * 32 + lrow, ch));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bq[kk % PF][j], acc[i][j], 0, 0, 0);
+    if (kk + PF < KS) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        bq[kk % PF][j] = *reinterpret_cast<const bf16x8*>(hsrc + ((size_t)j * KS + kk + PF) * 512);
+    }
   }
+  __syncthreads();   // every wave is done reading Y
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int lr = i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-      const int row = row_base + lr;
-      if (row >= out_rows) continue;
-      const bool live = row_has_window(plan, B, row);
+      const bool lv = row_live[lr] != 0;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int col = nbase + j * 32 + lrow;
-        out[(size_t)row * D + col] = live ? f2bf(acc[i][j][r]) : uint16_t(0);
+        const int col = (cb0 + j) * 32 + lrow;
+        *reinterpret_cast<uint16_t*>(smem + post_lds<D>(lr, col >> 3) + (col & 7) * 2) =
+            lv ? f2bf(acc[i][j][r]) : uint16_t(0);
       }
     }
+  __syncthreads();
+  constexpr int CHUNKS = D / 8;             // 16-byte chunks per row
+#pragma unroll
+  for (int it = 0; it < POST_ROWS * CHUNKS / 256; ++it) {
+    const int q = it * 256 + (int)threadIdx.x;
+    const int lr = q / CHUNKS, ch = q - lr * CHUNKS;
+    const int row = row_base + lr;
+    if (row < out_rows)
+      *reinterpret_cast<uint4*>(out + (size_t)row * D + ch * 8) =
+          *reinterpret_cast<const uint4*>(smem + post_lds<D>(lr, ch));
+  }
 }
 
-// HadT[n][k] = Had[k][n] (D x D bf16), through a 32 x 32 LDS tile.
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
-                                                             uint16_t* __restrict__ outT, int D) {
-  __shared__ uint16_t tile[32][33];
-  const int bx = blockIdx.x * 32, by = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 8 rows per pass
-  for (int y = ty; y < 32; y += 8) tile[y][tx] = in[(size_t)(by + y) * D + bx + tx];
-  __syncthreads();
-  for (int y = ty; y < 32; y += 8) outT[(size_t)(bx + y) * D + by + tx] = tile[tx][y];
+// Had (D x D bf16, row k, column n) in the fragment-major order of the MFMA B
+// operand: fragment (column block cb, k-step kk) is 64 lanes x 8 values, lane
+// l holding column cb*32 + l%32 and rows kk*16 + 8*(l/32) .. +8.  One thread
+// per lane piece; D*D/8 pieces.
+__global__ __launch_bounds__(256) void hadamard_pack_kernel(const uint16_t* __restrict__ had,
+                                                            uint16_t* __restrict__ hadF, int D) {
+  const int o = blockIdx.x * 256 + threadIdx.x;
+  if (o >= D * D / 8) return;
+  const int lane = o & 63, f = o >> 6;
+  const int ks = D / 16;
+  const int cb = f / ks, kk = f - cb * ks;
+  const int n = cb * 32 + (lane & 31), k0 = kk * 16 + 8 * (lane >> 5);
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = had[(size_t)(k0 + e) * D + n];
+  *reinterpret_cast<uint4*>(hadF + (size_t)o * 8) =
+      make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
 }
 
 // ---------------------------------------------------------------------------

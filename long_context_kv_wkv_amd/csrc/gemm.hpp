@@ -6,21 +6,20 @@
 //
 // Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2, each wave a
 // 128 x 128 sub-tile = 4 x 4 blocks of the 32x32x16 bf16 MFMA, accumulators
-// in AGPRs), K step 64, two 64 KiB LDS stages filled by direct-to-LDS copies
+// in AGPRs), K step 32, four 32 KiB LDS stages filled by direct-to-LDS copies
 // (global_load_lds_dwordx4: no staging registers, no ds_write).
-//  * X tile: row-major in LDS, 128 B per row, 16-byte chunks XOR-swizzled by
-//    (row & 7) ^ ((row >> 3) & 1) so fragment reads are bank-conflict free
-//    whether LDS serves 8 or 16 lanes per cycle.  A copy instruction covers 8
-//    rows x 128 B (one cache line per row); each lane fetches the logical chunk
-//    the swizzle places at its LDS slot.
+//  * X tile: row-major in LDS, 64 B per row, 16-byte chunks XOR-swizzled by
+//    ((row >> 1) ^ (row >> 2)) & 3 so fragment reads are bank conflict free
+//    whether LDS serves 8 or 16 lanes per cycle.  A copy instruction covers
+//    16 rows x 64 B; each lane fetches the logical chunk the swizzle places
+//    at its LDS slot.
 //  * Panel tile: fragment-major like the panel in HBM (1 KiB per MFMA B
 //    fragment), copied and read lane-contiguously.
-// Per K step the 16 copies of the next tile are interleaved one per two MFMAs
-// in the first half of the step, while the second half's fragments are read;
-// the second half's MFMAs then cover the copies' latency before the single
-// wait + barrier of the step.  (Measured on MI355X: the copy stream, not the
-// MFMA rate, bounds this kernel; bursts of copies stall issue, deeper stage
-// counts lower the copy rate.)
+// Copies run three K steps ahead of the MFMAs: on MI355X one step of MFMA
+// work (~0.5 us) is shorter than the latency of a batch of copies (~1.2 us
+// measured), so fewer stages leave the MFMAs waiting; the stage count is
+// what 128 KiB of LDS holds at this K step.  The 8 copies of a step are
+// interleaved one per two MFMAs in its first half.
 //
 // The tile schedule and the epilogue live in pool.hpp (the GEMM never writes
 // the projection to HBM: its epilogue pools windows straight from the
@@ -30,11 +29,13 @@
 
 namespace cmp {
 
-constexpr int GM_BM = 256, GM_BN = 256, GM_BK = 64;
+constexpr int GM_BM = 256, GM_BN = 256, GM_BK = 32;
 constexpr int GM_THREADS = 256;
-constexpr int GM_STAGES = 2;
-constexpr int GM_STAGE_BYTES = (GM_BM + GM_BN) * GM_BK * 2;   // 64 KiB
+constexpr int GM_STAGES = 4;
+constexpr int GM_STAGE_BYTES = (GM_BM + GM_BN) * GM_BK * 2;   // 32 KiB
 constexpr int GM_LDS_BYTES = GM_STAGES * GM_STAGE_BYTES;     // 128 KiB
+constexpr int GM_A_COPIES = GM_BM * GM_BK * 2 / 1024 / 4;     // X copies per wave and stage
+constexpr int GM_A_ROWS = 1024 / (GM_BK * 2);                 // X rows per copy instruction
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -42,36 +43,42 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)l, 16, 0, 0);
 }
-// byte offset of 16-byte chunk `chunk` of row `row` in a 128-byte-row tile
+// byte offset of 16-byte chunk `chunk` of row `row` in a 64-byte-row tile
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return (row << 7) + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+  return (row << 6) + ((chunk ^ (((row >> 1) ^ (row >> 2)) & 3)) << 4);
+}
+// Tile row that copy instruction j of `wave` fills for `lane`.
+__device__ __forceinline__ int gm_copy_row(int wave, int lane, int j) {
+  return (wave * GM_A_COPIES + j) * GM_A_ROWS + lane / (GM_BK / 8);
 }
 
 // ---------------------------------------------------------------------------
 // Main loop of one 256 x 256 tile: acc[i][j] (wave (wm, wn), 32x32 block i of
 // its 128 rows, block j of its 128 columns) += X[rows] . Wp[n0 .. n0+256)^T.
-// arow[j] is the packed X row that this lane's j-th copy instruction reads:
-// tile row ((wave * 8 + j) * 8 + lane / 8); rows outside the tensor must be
-// clamped by the caller to any valid row (their results are not used).
+// arow[j] is the X row that this lane's j-th copy instruction reads (tile row
+// gm_copy_row(wave, lane, j)); rows outside the tensor must be clamped by the
+// caller to any valid row (their results are not used).  K % 32 == 0 and
+// K >= 96.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], uint8_t* smem,
                                               const uint16_t* __restrict__ X,
                                               const uint16_t* __restrict__ W, int K, int n0,
-                                              const int (&arow)[8]) {
+                                              const int (&arow)[GM_A_COPIES]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  // A copies: instruction j of wave w fills tile rows r0 = (8w + j) * 8 .. +8;
-  // lane l lands at LDS byte r0*128 + 16 l, i.e. row r0 + l/8, physical chunk
-  // l%8, so it fetches the logical chunk that the swizzle places there.
-  const uint16_t* asrc[8];
+  // X copies: instruction j of wave w fills tile rows r0 = (4w + j) * 16 ..
+  // +16; lane l lands at LDS byte r0*64 + 16 l, i.e. row r0 + l/4, physical
+  // chunk l%4, so it fetches the logical chunk the swizzle places there.
+  const uint16_t* asrc[GM_A_COPIES];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = (wave * 8 + j) * 8 + (lane >> 3);
-    const int kc = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
+  for (int j = 0; j < GM_A_COPIES; ++j) {
+    const int row = gm_copy_row(wave, lane, j);
+    const int kc = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
     asrc[j] = X + (size_t)arow[j] * K + kc * 8;
   }
-  // B copies: fragment f = 8w + j of the stage is (column block f / 4, k-step f % 4)
+  // panel copies: fragment f = 4w + j of the stage is (column block f / 2,
+  // k-step f % 2)
   const size_t ksteps = (size_t)(K >> 4);
   const uint16_t* bsrc = W + ((((size_t)(n0 >> 5) + 2 * wave) * ksteps) * 64 + lane) * 8;
 
@@ -86,74 +93,82 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], uint8_t* smem
   const int KT = K / GM_BK;
 #define WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | 0x0f70)
 #define BARRIER() asm volatile("s_barrier" ::: "memory")
-  {
+#define ISSUE(KT_, ST_)                                                            \
+  {                                                                                \
+    uint8_t* st_ = smem + (ST_) * GM_STAGE_BYTES;                                  \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                \
+      dma16(asrc[j] + (KT_) * GM_BK, st_ + (wave * 4 + j) * 1024);                 \
+      dma16(bsrc + ((size_t)(j >> 1) * ksteps + (KT_) * 2 + (j & 1)) * 512,        \
+            st_ + 16384 + (wave * 4 + j) * 1024);                                  \
+    }                                                                              \
+  }
+  // s_waitcnt vmcnt(12) lgkmcnt(0)
+#define WAIT_VM12_LGKM0() __builtin_amdgcn_s_waitcnt((12 & 0xf) | ((12 >> 4) << 14) | 0x0070)
+  ISSUE(0, 0);
+  ISSUE(1, 1);
+  ISSUE(2, 2);
+  WAIT_VM(16);
+  BARRIER();
+  // Fragments: a0/b0 = k-step 0 of the current stage, a1/b1 = k-step 1.
+  // Each half-step's MFMAs run while the other half's fragments are read,
+  // so no LDS read latency is exposed; the one barrier per step sits
+  // between the halves.  The step's 8 copies (of step kt+3) are spread one
+  // per 4 MFMAs over both halves, each group fenced so the compiler cannot
+  // bunch them: a burst of copies from all waves stalls their issue.
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      dma16(asrc[j], smem + (wave * 8 + j) * 1024);
-      dma16(bsrc + ((size_t)(j >> 2) * ksteps + (j & 3)) * 512, smem + 32768 + (wave * 8 + j) * 1024);
+  for (int i = 0; i < 4; ++i) {
+    a0[i] = *reinterpret_cast<const bf16x8*>(smem + swz(wm * 128 + i * 32 + lrow, lhalf));
+    b0[i] = *reinterpret_cast<const bf16x8*>(smem + 16384 + ((wn * 4 + i) * 2) * 1024 + lane * 16);
+  }
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint8_t* sa = smem + (kt & 3) * GM_STAGE_BYTES;
+    const uint8_t* sb = sa + 16384;
+    const uint8_t* na = smem + ((kt + 1) & 3) * GM_STAGE_BYTES;
+    const uint8_t* nb = na + 16384;
+    // copies of step kt+3 go to the stage of step kt-1, which every wave
+    // finished reading before the previous step's barrier (the last steps
+    // re-copy step KT-1 into stages nothing reads any more)
+    const int kn = min(kt + 3, KT - 1);
+    uint8_t* st = smem + ((kt + 3) & 3) * GM_STAGE_BYTES;
+    const uint16_t* bk = bsrc + (size_t)kn * 2 * 512;
+    // first half: copies 0-3 (A rows), reads of a1/b1, MFMAs of a0 x b0
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+      dma16(asrc[g] + kn * GM_BK, st + (wave * 4 + g) * 1024);
+      a1[g] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + g * 32 + lrow, 2 + lhalf));
+      b1[g] = *reinterpret_cast<const bf16x8*>(sb + ((wn * 4 + g) * 2 + 1) * 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[g], b0[j], acc[g][j], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // step kt+1's stage: this wave's copies are done when only the 12 issued
+    // after them (step kt+2's and half of step kt+3's) are outstanding, and
+    // the barrier publishes every wave's (a bare barrier: a workgroup fence
+    // would wait for every copy)
+    WAIT_VM12_LGKM0();
+    BARRIER();
+    // second half: copies 4-7 (panel fragments), reads of the next a0/b0,
+    // MFMAs of a1 x b1
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+      dma16(bk + ((size_t)(g >> 1) * ksteps + (g & 1)) * 512, st + 16384 + (wave * 4 + g) * 1024);
+      a0[g] = *reinterpret_cast<const bf16x8*>(na + swz(wm * 128 + g * 32 + lrow, lhalf));
+      b0[g] = *reinterpret_cast<const bf16x8*>(nb + ((wn * 4 + g) * 2) * 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[g], b1[j], acc[g][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   WAIT_VM(0);
   BARRIER();
-  for (int kt = 0; kt < KT; ++kt) {
-    // the next tile's copies go to the other stage, which every wave finished
-    // reading before the last barrier (the last iteration re-copies tile
-    // KT-1 there; nothing reads it)
-    const int kn = min(kt + 1, KT - 1);
-    uint8_t* stn = smem + ((kt + 1) & 1) * GM_STAGE_BYTES;
-    const uint8_t* sa = smem + (kt & 1) * GM_STAGE_BYTES;
-    const uint8_t* sb = sa + 32768;
-    bf16x8 a[4][4], b[4][4];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[kk][i] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + i * 32 + lrow, kk * 2 + lhalf));
-        b[kk][i] = *reinterpret_cast<const bf16x8*>(sb + ((wn * 4 + i) * 4 + kk) * 1024 + lane * 16);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    // first half: all copies of the next tile interleaved with 32 MFMAs, and
-    // the second half's fragments read from LDS
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      dma16(asrc[j] + kn * GM_BK, stn + (wave * 8 + j) * 1024);
-      dma16(bsrc + ((size_t)(j >> 2) * ksteps + (kn * GM_BK >> 4) + (j & 3)) * 512,
-            stn + 32768 + (wave * 8 + j) * 1024);
-    }
-#pragma unroll
-    for (int kk = 2; kk < 4; ++kk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[kk][i] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + i * 32 + lrow, kk * 2 + lhalf));
-        b[kk][i] = *reinterpret_cast<const bf16x8*>(sb + ((wn * 4 + i) * 4 + kk) * 1024 + lane * 16);
-      }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][i], b[kk][j], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one copy
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 2; kk < 4; ++kk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][i], b[kk][j], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    WAIT_VM(0);
-    BARRIER();
-  }
+#undef ISSUE
 #undef WAIT_VM
+#undef WAIT_VM12_LGKM0
 #undef BARRIER
 }
 

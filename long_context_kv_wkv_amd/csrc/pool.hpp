@@ -171,10 +171,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
   const int P0 = R * (s / R) + tloc * GM_BM;
   const int n0 = nt * GM_BN;
 
-  int arow[8];
+  int arow[GM_A_COPIES];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int p = P0 + (wave * 8 + j) * 8 + (lane >> 3);
+  for (int j = 0; j < GM_A_COPIES; ++j) {
+    const int p = P0 + gm_copy_row(wave, lane, j);
     arow[j] = min(max(row0 + (p - s), 0), T - 1);
   }
   f32x16 acc[4][4];

@@ -59,14 +59,99 @@ __device__ __forceinline__ int gm_copy_row(int wave, int lane, int j) {
 // gm_copy_row(wave, lane, j)); rows outside the tensor must be clamped by the
 // caller to any valid row (their results are not used).  K % 32 == 0 and
 // K >= 96.
+//
+// Schedule of a K step (32 MFMAs per wave in 8 groups of 4): each group
+// issues one copy of step kt+3 and two LDS fragment reads.  The first half's
+// MFMAs use k-step 0 of the stage while k-step 1 is read, the second half's
+// use k-step 1 while the next stage's k-step 0 is read, and the single
+// barrier of the step sits between the halves, so no LDS read latency is
+// exposed.  The copy unit takes a 1 KiB copy every few tens of cycles and a
+// wave cannot issue past a copy it has not accepted, so the waves place
+// their copy at different MFMAs of the group (wave w after MFMA w): copies
+// from the lock-stepped waves reach the unit one after another instead of
+// together.  Every group is fenced so the compiler keeps this order.
 // ---------------------------------------------------------------------------
+#define GM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | 0x0f70)
+// s_waitcnt vmcnt(12) lgkmcnt(0)
+#define GM_WAIT_VM12_LGKM0() __builtin_amdgcn_s_waitcnt((12 & 0xf) | ((12 >> 4) << 14) | 0x0070)
+#define GM_BARRIER() asm volatile("s_barrier" ::: "memory")
+
+template <int P>
+__device__ __forceinline__ void gemm_steps(f32x16 (&acc)[4][4], uint8_t* smem,
+                                           const uint16_t* const (&asrc)[GM_A_COPIES],
+                                           const uint16_t* __restrict__ bsrc, size_t ksteps,
+                                           int KT) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  // Fragments: a0/b0 = k-step 0 of the current stage, a1/b1 = k-step 1.
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a0[i] = *reinterpret_cast<const bf16x8*>(smem + swz(wm * 128 + i * 32 + lrow, lhalf));
+    b0[i] = *reinterpret_cast<const bf16x8*>(smem + 16384 + ((wn * 4 + i) * 2) * 1024 + lane * 16);
+  }
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint8_t* sa = smem + (kt & 3) * GM_STAGE_BYTES;
+    const uint8_t* sb = sa + 16384;
+    const uint8_t* na = smem + ((kt + 1) & 3) * GM_STAGE_BYTES;
+    const uint8_t* nb = na + 16384;
+    // copies of step kt+3 go to the stage of step kt-1, which every wave
+    // finished reading before the previous step's barrier (the last steps
+    // re-copy step KT-1 into stages nothing reads any more)
+    const int kn = min(kt + 3, KT - 1);
+    uint8_t* st = smem + ((kt + 3) & 3) * GM_STAGE_BYTES;
+    const uint16_t* bk = bsrc + (size_t)kn * 2 * 512;
+    // first half: copies 0-3 (X rows), reads of a1/b1, MFMAs of a0 x b0
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+      a1[g] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + g * 32 + lrow, 2 + lhalf));
+      b1[g] = *reinterpret_cast<const bf16x8*>(sb + ((wn * 4 + g) * 2 + 1) * 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j == P) {
+          __builtin_amdgcn_sched_barrier(0);
+          dma16(asrc[g] + kn * GM_BK, st + (wave * 4 + g) * 1024);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[g], b0[j], acc[g][j], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // step kt+1's stage: this wave's copies are done when only the 12 issued
+    // after them (step kt+2's and half of step kt+3's) are outstanding, and
+    // the barrier publishes every wave's (a bare barrier: a workgroup fence
+    // would wait for every copy)
+    GM_WAIT_VM12_LGKM0();
+    GM_BARRIER();
+    // second half: copies 4-7 (panel fragments), reads of the next a0/b0,
+    // MFMAs of a1 x b1
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+      a0[g] = *reinterpret_cast<const bf16x8*>(na + swz(wm * 128 + g * 32 + lrow, lhalf));
+      b0[g] = *reinterpret_cast<const bf16x8*>(nb + ((wn * 4 + g) * 2) * 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j == P) {
+          __builtin_amdgcn_sched_barrier(0);
+          dma16(bk + ((size_t)(g >> 1) * ksteps + (g & 1)) * 512, st + 16384 + (wave * 4 + g) * 1024);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[g], b1[j], acc[g][j], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], uint8_t* smem,
                                               const uint16_t* __restrict__ X,
                                               const uint16_t* __restrict__ W, int K, int n0,
                                               const int (&arow)[GM_A_COPIES]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
   // X copies: instruction j of wave w fills tile rows r0 = (4w + j) * 16 ..
   // +16; lane l lands at LDS byte r0*64 + 16 l, i.e. row r0 + l/4, physical
   // chunk l%4, so it fetches the logical chunk the swizzle places there.
@@ -89,87 +174,32 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[4][4], uint8_t* smem
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int lrow = lane & 31, lhalf = lane >> 5;
   const int KT = K / GM_BK;
-#define WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | 0x0f70)
-#define BARRIER() asm volatile("s_barrier" ::: "memory")
-#define ISSUE(KT_, ST_)                                                            \
-  {                                                                                \
-    uint8_t* st_ = smem + (ST_) * GM_STAGE_BYTES;                                  \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                \
-      dma16(asrc[j] + (KT_) * GM_BK, st_ + (wave * 4 + j) * 1024);                 \
-      dma16(bsrc + ((size_t)(j >> 1) * ksteps + (KT_) * 2 + (j & 1)) * 512,        \
-            st_ + 16384 + (wave * 4 + j) * 1024);                                  \
-    }                                                                              \
-  }
-  // s_waitcnt vmcnt(12) lgkmcnt(0)
-#define WAIT_VM12_LGKM0() __builtin_amdgcn_s_waitcnt((12 & 0xf) | ((12 >> 4) << 14) | 0x0070)
-  ISSUE(0, 0);
-  ISSUE(1, 1);
-  ISSUE(2, 2);
-  WAIT_VM(16);
-  BARRIER();
-  // Fragments: a0/b0 = k-step 0 of the current stage, a1/b1 = k-step 1.
-  // Each half-step's MFMAs run while the other half's fragments are read,
-  // so no LDS read latency is exposed; the one barrier per step sits
-  // between the halves.  The step's 8 copies (of step kt+3) are spread one
-  // per 4 MFMAs over both halves, each group fenced so the compiler cannot
-  // bunch them: a burst of copies from all waves stalls their issue.
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  // the first three stages
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a0[i] = *reinterpret_cast<const bf16x8*>(smem + swz(wm * 128 + i * 32 + lrow, lhalf));
-    b0[i] = *reinterpret_cast<const bf16x8*>(smem + 16384 + ((wn * 4 + i) * 2) * 1024 + lane * 16);
-  }
-  for (int kt = 0; kt < KT; ++kt) {
-    const uint8_t* sa = smem + (kt & 3) * GM_STAGE_BYTES;
-    const uint8_t* sb = sa + 16384;
-    const uint8_t* na = smem + ((kt + 1) & 3) * GM_STAGE_BYTES;
-    const uint8_t* nb = na + 16384;
-    // copies of step kt+3 go to the stage of step kt-1, which every wave
-    // finished reading before the previous step's barrier (the last steps
-    // re-copy step KT-1 into stages nothing reads any more)
-    const int kn = min(kt + 3, KT - 1);
-    uint8_t* st = smem + ((kt + 3) & 3) * GM_STAGE_BYTES;
-    const uint16_t* bk = bsrc + (size_t)kn * 2 * 512;
-    // first half: copies 0-3 (A rows), reads of a1/b1, MFMAs of a0 x b0
+  for (int t = 0; t < 3; ++t) {
+    uint8_t* st = smem + t * GM_STAGE_BYTES;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      __builtin_amdgcn_sched_barrier(0);
-      dma16(asrc[g] + kn * GM_BK, st + (wave * 4 + g) * 1024);
-      a1[g] = *reinterpret_cast<const bf16x8*>(sa + swz(wm * 128 + g * 32 + lrow, 2 + lhalf));
-      b1[g] = *reinterpret_cast<const bf16x8*>(sb + ((wn * 4 + g) * 2 + 1) * 1024 + lane * 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[g], b0[j], acc[g][j], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      dma16(asrc[j] + t * GM_BK, st + (wave * 4 + j) * 1024);
+      dma16(bsrc + ((size_t)(j >> 1) * ksteps + t * 2 + (j & 1)) * 512, st + 16384 + (wave * 4 + j) * 1024);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // step kt+1's stage: this wave's copies are done when only the 12 issued
-    // after them (step kt+2's and half of step kt+3's) are outstanding, and
-    // the barrier publishes every wave's (a bare barrier: a workgroup fence
-    // would wait for every copy)
-    WAIT_VM12_LGKM0();
-    BARRIER();
-    // second half: copies 4-7 (panel fragments), reads of the next a0/b0,
-    // MFMAs of a1 x b1
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      __builtin_amdgcn_sched_barrier(0);
-      dma16(bk + ((size_t)(g >> 1) * ksteps + (g & 1)) * 512, st + 16384 + (wave * 4 + g) * 1024);
-      a0[g] = *reinterpret_cast<const bf16x8*>(na + swz(wm * 128 + g * 32 + lrow, lhalf));
-      b0[g] = *reinterpret_cast<const bf16x8*>(nb + ((wn * 4 + g) * 2) * 1024 + lane * 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[g], b1[j], acc[g][j], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   }
-  WAIT_VM(0);
-  BARRIER();
-#undef ISSUE
-#undef WAIT_VM
-#undef WAIT_VM12_LGKM0
-#undef BARRIER
+  GM_WAIT_VM(16);
+  GM_BARRIER();
+  switch (__builtin_amdgcn_readfirstlane(wave)) {
+    case 0: gemm_steps<0>(acc, smem, asrc, bsrc, ksteps, KT); break;
+    case 1: gemm_steps<1>(acc, smem, asrc, bsrc, ksteps, KT); break;
+    case 2: gemm_steps<2>(acc, smem, asrc, bsrc, ksteps, KT); break;
+    default: gemm_steps<3>(acc, smem, asrc, bsrc, ksteps, KT); break;
+  }
+  // every copy has landed (the epilogue reuses the LDS)
+  GM_WAIT_VM(0);
+  GM_BARRIER();
 }
+
+#undef GM_WAIT_VM
+#undef GM_WAIT_VM12_LGKM0
+#undef GM_BARRIER
 
 }  // namespace cmp

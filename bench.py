@@ -123,9 +123,10 @@ def bench_decode(name, steps, warmup, copies=12):
     return dict(us_per_step=us, kernels_us=kern, panel_bytes=panel_bytes)
 
 
-def cpu_baseline(w, budget_s=12.0):
+def cpu_baseline(w, budget_s=20.0):
     """The oracle, untuned, on a bounded sample of the 128K workload: whole
-    windows (projection of their rows, pooling, RMSNorm, RoPE, Hadamard)."""
+    windows (projection of their rows, pooling, RMSNorm, RoPE, Hadamard),
+    as many as fit the time budget (at most every window of the workload)."""
     from oracle import compressor_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -133,11 +134,19 @@ def cpu_baseline(w, budget_s=12.0):
     except Exception:
         threads = 1
     rng = np.random.default_rng(0)
-    n = 32
-    t0 = time.perf_counter()
-    O.compressor(w, windows=rng.choice(w["out_rows"], n, replace=False), project_all=False)
-    dt = time.perf_counter() - t0
-    n2 = int(max(n, min(4096, n * budget_s / max(dt, 1e-3))))
+
+    def run(n):
+        t0 = time.perf_counter()
+        O.compressor(w, windows=rng.choice(w["out_rows"], n, replace=False), project_all=False)
+        return time.perf_counter() - t0
+
+    # a call has a fixed part (the whole output and pool arrays) and a part per
+    # window: size the sample from both
+    na, nb = 32, 512
+    ta, tb = run(na), run(nb)
+    per = max((tb - ta) / (nb - na), 1e-6)
+    fixed = max(ta - na * per, 0.0)
+    n2 = int(max(nb, min(w["out_rows"], (budget_s - fixed) / per)))
     t0 = time.perf_counter()
     O.compressor(w, windows=rng.choice(w["out_rows"], n2, replace=False), project_all=False)
     dt2 = time.perf_counter() - t0
@@ -146,6 +155,96 @@ def cpu_baseline(w, budget_s=12.0):
             "sample": f"{n2} random windows of the 128K C4A workload (their 8 projected rows "
                       f"each, pooling, RMSNorm, RoPE, Hadamard) plus the state rows, fp64 numpy, "
                       f"{dt2:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+# Profile summaries (run on the host after the rocprofv3 runs listed in
+# PROFILE_COMMANDS; they read the CSV files those runs leave under a folder)
+# ---------------------------------------------------------------------------
+PROFILE_COMMANDS = {
+    "kt": "rocprofv3 --kernel-trace --stats -T --output-format csv -d {out}/kt -o run -- "
+          "python3 bench.py --steps 5 --warmup 1 --decode-steps 50 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -T --output-format csv -d {out}/fetch -o run -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE -T --output-format csv -d {out}/write -o run -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline",
+    "cfetch": "rocprofv3 --pmc FETCH_SIZE -T --output-format csv -d {out}/cfetch -o run -- "
+              "python3 bench.py --copy-calibration",
+    "cwrite": "rocprofv3 --pmc WRITE_SIZE -T --output-format csv -d {out}/cwrite -o run -- "
+              "python3 bench.py --copy-calibration",
+}
+GEMM_KERNEL = "gemm_pool_kernel"
+
+
+def _find_csv(folder, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {folder}")
+    return hits[0]
+
+
+def _counter_values(folder, counter, kernel_part):
+    import csv
+    vals = []
+    for r in csv.DictReader(open(_find_csv(folder, "counter_collection.csv"))):
+        if r["Counter_Name"] == counter and kernel_part in r["Kernel_Name"]:
+            vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def summarize_profiles(out):
+    """Write profiles/bench_kernel_stats.md and profiles/gemm_c4a_128k_traffic.json
+    from the CSV files of the PROFILE_COMMANDS runs under `out`."""
+    import csv
+    sha = kernel_source_sha("gemm.hpp", "pool.hpp", "common.hpp")
+    rows = list(csv.DictReader(open(_find_csv(os.path.join(out, "kt"), "kernel_stats.csv"))))
+    lines = ["# Kernel-time summary: bench.py (128K C4A prefill + 32-request decode)", "",
+             "Command (from the repository root, on one MI355X):", "", "```",
+             PROFILE_COMMANDS["kt"].format(out="gpurun_out"), "```", "",
+             "The prefill kernels run 6 times (1 warm-up + 5 timed; the per-kernel event pass "
+             "adds 5 more); the decode kernels run for 4 workloads x (warm-up + timed + "
+             "event-timed) steps.  Durations in ns.", "",
+             "| kernel | calls | total ns | average ns | % | min ns | max ns |",
+             "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].split("(")[0].replace("void ", "")
+        name = name.split("<")[0].split("::")[-1][:60]
+        lines.append(f"| {name} | {r['Calls']} | {r['TotalDurationNs']} | "
+                     f"{float(r['AverageNs']):.0f} | {float(r['Percentage']):.2f} | "
+                     f"{r['MinNs']} | {r['MaxNs']} |")
+    lines += ["", f"Kernel source hash (gemm.hpp + pool.hpp + common.hpp): `{sha}`."]
+    open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w").write("\n".join(lines) + "\n")
+
+    fetch = _counter_values(os.path.join(out, "fetch"), "FETCH_SIZE", GEMM_KERNEL)
+    write = _counter_values(os.path.join(out, "write"), "WRITE_SIZE", GEMM_KERNEL)
+    cfetch = _counter_values(os.path.join(out, "cfetch"), "FETCH_SIZE", "copy")
+    cwrite = _counter_values(os.path.join(out, "cwrite"), "WRITE_SIZE", "copy")
+    copy_bytes = 1 << 30
+    # counters are KiB per dispatch; a plain copy of known size fixes the scale
+    fscale = copy_bytes / (np.median(cfetch) * 1024.0)
+    wscale = copy_bytes / (np.median(cwrite) * 1024.0)
+    fb = float(np.median(fetch)) * 1024.0 * fscale
+    wb = float(np.median(write)) * 1024.0 * wscale
+    doc = {
+        "kernel": GEMM_KERNEL,
+        "workload": "c4a_128k prefill (T=131072, H=7168, N=2048)",
+        "kernel_source_sha": sha,
+        "fetch_size_kib_per_dispatch": fetch,
+        "write_size_kib_per_dispatch": write,
+        "copy_calibration": {"bytes": copy_bytes, "fetch_size_kib": cfetch,
+                             "write_size_kib": cwrite, "fetch_scale": fscale,
+                             "write_scale": wscale},
+        "fetch_bytes_per_launch": fb,
+        "write_bytes_per_launch": wb,
+        "hbm_bytes_per_launch": fb + wb,
+        "commands": [PROFILE_COMMANDS[k].format(out="gpurun_out")
+                     for k in ("fetch", "write", "cfetch", "cwrite")],
+    }
+    json.dump(doc, open(os.path.join(ROOT, "profiles", "gemm_c4a_128k_traffic.json"), "w"),
+              indent=1)
+    print(json.dumps({"kernel_stats_rows": len(rows), "hbm_bytes_per_launch": fb + wb,
+                      "sha": sha}))
 
 
 def main():
@@ -160,10 +259,15 @@ def main():
                     help="time only the decode workloads (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (scales HBM byte counters)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="host only: write profiles/ summaries from rocprofv3 CSVs under DIR")
     a = ap.parse_args()
+    if a.summarize_profiles:
+        summarize_profiles(a.summarize_profiles)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -188,7 +292,7 @@ def main():
     flops = 2.0 * T * H * N
     achieved = flops / (gemm_ms * 1e-3) / 1e12
     sha = kernel_source_sha("gemm.hpp", "pool.hpp", "common.hpp")
-    traffic = load_traffic("gemm_c4a_128k_traffic.json", sha)
+    traffic = load_traffic("gemm_c4a_128k_traffic.json", sha)   # bytes per launch, or None
     result = {
         "metric": "compressed tokens/s for 128K-token C4A prefill (T=131072, H=7168, D=512, "
                   "ratio 4, rotate); also us per 32-request decode",

@@ -83,9 +83,29 @@ def bench_prefill(steps, warmup):
                 device=torch.cuda.get_device_name(0))
 
 
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one decode step: the panel, x, the ring rows a
+    completing window reads (kv and score of its channel set), the state rows
+    written, the output rows."""
+    r, coff, D, H, B = w["ratio"], w["coff"], w["head_dim"], w["hidden"], w["batch"]
+    N = 2 * coff * D
+    total = N * H * 2 + B * H * 2 + w["out_rows"] * D * 2
+    seq = w["seqused"] if w["seqused"] is not None else np.ones(B, np.int32)
+    for b in range(B):
+        if seq[b] != 1:
+            continue
+        s = int(w["start_pos"][b])
+        e = s + 1
+        if e % r == 0:
+            total += (coff * r - 1) * D * 8          # the window's other slots, kv + score
+        if max(s, r * (e // r) - (coff - 1) * r) <= s:
+            total += coff * D * 8                    # the token's state row
+    return total
+
+
 def bench_decode(name, steps, warmup, copies=12):
-    """Decode step time with `copies` distinct weight panels / inputs rotated
-    so that the 256 MB last-level cache cannot hold the streamed panel."""
+    """Decode step time with `copies` distinct weight panels, inputs and state
+    pools rotated so that the 256 MB last-level cache cannot hold them."""
     import torch
     import gpu_harness
     import long_context_kv_wkv_amd as cmp
@@ -95,32 +115,58 @@ def bench_decode(name, steps, warmup, copies=12):
     case = gpu_harness.DeviceCase(w)
     panels = [case.w_packed] + [case.w_packed.clone() for _ in range(copies - 1)]
     xs = [case.x] + [case.x.clone() for _ in range(copies - 1)]
+    kvs = [case.kv_state] + [case.kv_state.clone() for _ in range(copies - 1)]
+    scs = [case.score_state] + [case.score_state.clone() for _ in range(copies - 1)]
 
     def run(i):
-        case.decode(w_packed=panels[i % copies], x=xs[i % copies])
+        j = i % copies
+        case.decode(w_packed=panels[j], x=xs[j], kv_state=kvs[j], score_state=scs[j])
 
     for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # host-driven steps (Python marshalling and launch per step), for context
     ev0.record()
     for i in range(steps):
         run(i)
     ev1.record()
     torch.cuda.synchronize()
-    us = ev0.elapsed_time(ev1) * 1000.0 / steps
+    us_eager = ev0.elapsed_time(ev1) * 1000.0 / steps
+    # device time per step: one step per copy captured in a HIP graph (the
+    # calls do no host sync, allocation or memset) and replayed
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for j in range(copies):
+            run(j)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // copies)
+    ev0.record()
+    for _ in range(reps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1000.0 / (reps * copies)
     # per-kernel durations in a second pass
     cmp.compressor_timing_enable(True)
     for i in range(steps):
         run(i)
     torch.cuda.synchronize()
     kern = {}
-    for k in ("gemv", "decode_tail"):
+    for k in ("decode_main", "decode_tail"):
         n, ms = cmp.compressor_timing_query(k)
         kern[k] = ms * 1000.0 / max(n, 1)
     cmp.compressor_timing_enable(False)
     panel_bytes = case.w_packed.numel() * 2
-    return dict(us_per_step=us, kernels_us=kern, panel_bytes=panel_bytes)
+    return dict(us_per_step=us, us_per_step_eager=us_eager, kernels_us=kern,
+                panel_bytes=panel_bytes, step_bytes=decode_bytes(w))
 
 
 def cpu_baseline(w, budget_s=20.0):
@@ -316,9 +362,12 @@ def main():
         dec = {}
         for name in ("decode_c4a", "decode_c128a", "decode_c4a_all", "decode_c128a_all"):
             d = bench_decode(name, a.decode_steps, 20)
-            gv = d["kernels_us"]["gemv"]
-            dec[name] = {"us_per_step": d["us_per_step"], "kernels_us": d["kernels_us"],
-                         "gemv_hbm_frac": d["panel_bytes"] / (gv * 1e-6) / 1e9 / PEAK_HBM_GBS}
+            dec[name] = {"us_per_step": d["us_per_step"],
+                         "us_per_step_eager": d["us_per_step_eager"],
+                         "kernels_us": d["kernels_us"],
+                         "algorithmic_bytes": d["step_bytes"],
+                         "hbm_frac": d["step_bytes"] / (d["us_per_step"] * 1e-6) / 1e9
+                         / PEAK_HBM_GBS}
         result["decode"] = dec
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)

@@ -201,7 +201,8 @@ const char* compressor_status_str(int status);
 /* Kernel timing: while enabled, every kernel the library enqueues is
  * bracketed by a pair of HIP events on the same stream.  Enabling clears the
  * records.  Kernel names: "plan", "hadamard_pack", "prefix", "gemm" (projection
- * with the window pooling and state stores in its epilogue), "post", "gemv",
+ * with the window pooling and state stores in its epilogue), "post",
+ * "decode_main" (GEMV and ring pre-pooling),
  * "decode_tail", "pack", "state_fill". */
 int compressor_timing_enable(int32_t on);
 

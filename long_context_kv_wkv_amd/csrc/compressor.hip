@@ -138,15 +138,18 @@ int decode_ksplit(const Cfg& cf) {
 constexpr int kDecodeMaxBatch = 64;
 
 struct DecodeLayout {
-  size_t err, partial, total;
-  int ks;
+  size_t err, partial, pp, ppflag, total;
+  int ks, split;
 };
 DecodeLayout decode_layout(const Cfg& cf, int B) {
   DecodeLayout L;
   L.ks = decode_ksplit(cf);
+  L.split = cf.ratio == 4 ? dec_split<4>() : dec_split<128>();
   size_t o = 0;
   L.err = o;       o += 256;
   L.partial = o;   o = align256(o + (size_t)L.ks * B * cf.N * 4);
+  L.pp = o;        o = align256(o + (size_t)B * L.split * 3 * cf.D * 4);
+  L.ppflag = o;    o = align256(o + (size_t)B * L.split * 4);
   L.total = o;
   return L;
 }
@@ -357,25 +360,27 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + L.err);
   float* partial = reinterpret_cast<float*>(ws + L.partial);
+  float* pp = reinterpret_cast<float*>(ws + L.pp);
+  int32_t* ppflag = reinterpret_cast<int32_t*>(ws + L.ppflag);
   const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
   const int B = a->batch;
   const int steps = cf.H / 16 / (L.ks * 4);
-  const dim3 gg(cf.N / 32, L.ks);
-  CMP_TRY(launch("gemv", st, [&] {
+  const dim3 gg(B * L.split + cf.N / 32 * L.ks);
+  CMP_TRY(launch("decode_main", st, [&] {
     const uint16_t* X = static_cast<const uint16_t*>(a->x);
     const uint16_t* W = static_cast<const uint16_t*>(a->w_packed);
-    if (B <= 32)
-      hipLaunchKernelGGL(gemv_kernel<1>, gg, dim3(GV_THREADS), 0, st, X, W, partial, B, cf.N,
-                         cf.H, steps, err);
-    else
-      hipLaunchKernelGGL(gemv_kernel<2>, gg, dim3(GV_THREADS), 0, st, X, W, partial, B, cf.N,
-                         cf.H, steps, err);
+    auto kern = cf.ratio == 4 ? (B <= 32 ? decode_main_kernel<1, 4, 2> : decode_main_kernel<2, 4, 2>)
+                              : (B <= 32 ? decode_main_kernel<1, 128, 1> : decode_main_kernel<2, 128, 1>);
+    hipLaunchKernelGGL(kern, gg, dim3(GV_THREADS), 0, st, cf, X, W, partial, B, steps, a->seqused,
+                       a->start_pos, a->kv_state, a->score_state, kvt, a->state_block_table, pp,
+                       ppflag, err);
   }));
   return launch("decode_tail", st, [&] {
     auto tail = cf.ratio == 4 ? decode_tail_kernel<4, 2> : decode_tail_kernel<128, 1>;
     hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, L.ks, B,
                        a->seqused, a->start_pos, a->ape, a->kv_state, a->score_state, kvt,
-                       a->state_block_table, static_cast<const uint16_t*>(a->norm_weight),
+                       a->state_block_table, pp, ppflag,
+                       static_cast<const uint16_t*>(a->norm_weight),
                        static_cast<const uint16_t*>(a->cos), static_cast<const uint16_t*>(a->sin),
                        static_cast<const uint16_t*>(a->hadamard), static_cast<uint16_t*>(a->out),
                        a->out_rows, err);

@@ -19,44 +19,159 @@ namespace cmp {
 
 constexpr int GV_THREADS = 256;
 
-// One run of U k16-steps: every weight and x fragment of the run is loaded
-// before the first MFMA of the run, so a wave keeps U * (1 + NRB) 16-byte
-// loads per lane in flight (the scheduler is fenced so it cannot interleave
-// them with the MFMAs to save registers).
+typedef __attribute__((address_space(3))) void dec_lds_t;
+typedef __attribute__((address_space(1))) void dec_glb_t;
+
+// One run of U k16-steps of a wave.  The x rows of the run go to the wave's
+// own LDS region by direct-to-LDS copies that each cover whole 16-byte-chunk
+// runs of rows (a row of the run is U*32 contiguous bytes), then the panel
+// fragments of the run are loaded (1 KiB contiguous each); once the copies
+// have landed, the x fragments are read from LDS and the MFMAs run.  Row t,
+// chunk c sits at t*U*32 + ((c ^ (t & 15)) * 16): the fragment reads (32
+// rows at one chunk index) are bank conflict free.  Rows >= B repeat row
+// B-1 (their results are not used).
 template <int U, int NRB>
 __device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp,
-                                         const uint16_t* const* __restrict__ xp, int s,
-                                         f32x16* acc) {
-  bf16x8 wf[U], xf[NRB][U];
+                                         const uint16_t* __restrict__ xk, int K, int B, int s,
+                                         uint8_t* xl, f32x16* acc) {
+  constexpr int CPR = 2 * U;             // 16-byte chunks per row of the run
+  constexpr int RPI = 64 / CPR;          // rows per copy instruction
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < NRB * U; ++j) {
+    const int t = j * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ (t & 15);
+    __builtin_amdgcn_global_load_lds((dec_glb_t*)(xk + (size_t)min(t, B - 1) * K + s * 16 + c * 8),
+                                     (dec_lds_t*)(xl + j * 1024), 16, 0, 0);
+  }
+  bf16x8 wf[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8*>(wp + (s + u) * 512);
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-    for (int u = 0; u < U; ++u) xf[rb][u] = *reinterpret_cast<const bf16x8*>(xp[rb] + (s + u) * 16);
+  // the copies were issued first: when only the U panel loads are
+  // outstanding, they have landed
+  __builtin_amdgcn_s_waitcnt((U & 0xf) | ((U >> 4) << 14) | 0x0f70);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-      acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[rb][u], wf[u], acc[rb], 0, 0, 0);
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int t = rb * 32 + (lane & 31);
+      const int c = 2 * u + (lane >> 5);
+      const bf16x8 xf = *reinterpret_cast<const bf16x8*>(xl + t * CPR * 16 + ((c ^ (t & 15)) << 4));
+      acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, wf[u], acc[rb], 0, 0, 0);
+    }
+  // the next run's copies overwrite the region: every read must be done
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
 }
 
-template <int NRB>
-__global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, float* __restrict__ partial,
-    int B, int N, int K, int steps_per_wave, uint32_t* __restrict__ err) {
-  __shared__ float red[4][NRB * 16][64];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *err = 0;   // this call's error word
-  const int i = lane & 31, h = lane >> 5;
-  const int kstep0 = (blockIdx.y * 4 + wave) * steps_per_wave;
-  const int kbeg = kstep0 * 16 + h * 8;
-  // fragment (column block blockIdx.x, k-step kstep0 + u) is 1 KiB contiguous
-  const uint16_t* wp = W + (((size_t)blockIdx.x * (K >> 4) + kstep0) * 64 + lane) * 8;
-  const uint16_t* xp[NRB];
+// Ring pre-pooling: workgroups of the decode main kernel that pool, for a
+// request whose token completes a window, every slot of that window except
+// the token itself ([PyPTO] 压缩窗口与状态更新; [CANN] 计算公式 steps 3-5):
+// per channel the softmax statistics (max m, sum l, weighted sum x) of those
+// slots.  None of them depends on this call's projection, so they run while
+// the GEMV streams the panel.  A C128A window (127 ring rows) is split over
+// DEC_SPLIT_C128 workgroups of 16 slots; a C4A window (7 ring rows) takes one.
+// Every load of a workgroup is issued before its first exponential.
+constexpr int DEC_SPLIT_C128 = 8;
+constexpr int DEC_MAX_KSPLIT = 20;           // K ranges of the GEMV (H / 512 at most)
+template <int R>
+constexpr int dec_split() { return R == 4 ? 1 : DEC_SPLIT_C128; }
+
+template <int R, int COFF>
+__device__ __forceinline__ void prepool_block(const Cfg& cf, int b, int sp,
+                                              const int32_t* __restrict__ seqused,
+                                              const int32_t* __restrict__ start_pos,
+                                              const float* __restrict__ kv_state,
+                                              const float* __restrict__ score_state,
+                                              const int32_t* __restrict__ kv_tab,
+                                              const int32_t* __restrict__ st_tab,
+                                              float* __restrict__ pp, int32_t* __restrict__ ppflag) {
+  constexpr int NSPLIT = dec_split<R>();
+  constexpr int NS = COFF * R / NSPLIT;          // slots per workgroup (8 or 16)
+  const int n = seqused ? seqused[b] : 1;
+  const int s = start_pos ? start_pos[b] : 0;
+  if (n != 1 || s < 0 || s == 0x7fffffff || (s + 1) % R != 0) return;   // nothing to pool
+  const int w = (s + 1) / R - 1;
+  const int D = cf.D, cD = COFF * D;
+  // slot j of the window: C4A j < 4 -> first set of position (w-1)*4 + j,
+  // j >= 4 -> second set of position w*4 + j - 4; C128A -> position w*128 + j
+  long rk[NS], rs[NS];
+  bool use[NS];
+  uint32_t bad = 0;
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) xp[rb] = X + (size_t)min(rb * 32 + i, B - 1) * K + kbeg;
+  for (int q = 0; q < NS; ++q) {
+    const int j = sp * NS + q;
+    const int cs = COFF == 2 ? (j >= R) : 0;
+    const int p = COFF == 2 ? (w - 1 + cs) * R + (j - cs * R) : w * R + j;
+    use[q] = p >= 0 && p != s;
+    rk[q] = 0;
+    rs[q] = 0;
+    if (use[q] && (!state_row(cf, kv_tab, b, p, &rk[q]) || !state_row(cf, st_tab, b, p, &rs[q]))) {
+      bad |= CMP_DEVERR_TABLE;
+      use[q] = false;
+    }
+  }
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float kv[NS], z[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+      const int j = sp * NS + q;
+      const int cs = COFF == 2 ? (j >= R) : 0;
+      kv[q] = use[q] ? kv_state[rk[q] * cD + cs * D + c] : 0.f;
+      z[q] = use[q] ? score_state[rs[q] * cD + cs * D + c] : -INFINITY;
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) m = fmaxf(m, z[q]);
+    float l = 0.f, x = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        const float e = __expf(z[q] - m);      // exp(-inf) = 0 for empty slots
+        l += e;
+        x = fmaf(e, kv[q], x);
+      }
+    }
+    float* o = pp + ((size_t)(b * NSPLIT + sp) * 3) * D + c;
+    o[0] = m;
+    o[D] = l;
+    o[2 * D] = x;
+  }
+  if (threadIdx.x == 0) ppflag[b * NSPLIT + sp] = (int32_t)bad;
+}
+
+// Decode main kernel.  Workgroups [0, B * split) pre-pool ring windows
+// (prepool_block); the rest run the GEMV: workgroup g owns column block
+// g % (N / 32) and K range g / (N / 32), its 4 waves divide the range, reduce
+// through LDS in a fixed order and write one fp32 partial per K range.
+template <int NRB, int R, int COFF>
+__global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
+    Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+    float* __restrict__ partial, int B, int steps_per_wave,
+    const int32_t* __restrict__ seqused, const int32_t* __restrict__ start_pos,
+    const float* __restrict__ kv_state, const float* __restrict__ score_state,
+    const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
+    float* __restrict__ pp, int32_t* __restrict__ ppflag, uint32_t* __restrict__ err) {
+  // per wave: the x rows of a run, then (after the runs) its accumulators
+  __shared__ __attribute__((aligned(1024))) uint8_t xstage[4][NRB * 32 * 16 * 32];
+  constexpr int NSPLIT = dec_split<R>();
+  const int npre = B * NSPLIT;
+  if ((int)blockIdx.x < npre) {
+    prepool_block<R, COFF>(cf, blockIdx.x / NSPLIT, blockIdx.x % NSPLIT, seqused, start_pos,
+                           kv_state, score_state, kv_tab, st_tab, pp, ppflag);
+    return;
+  }
+  const int g = blockIdx.x - npre;
+  const int N = cf.N, K = cf.H;
+  const int ncb = N / 32;
+  const int cb = g % ncb, kr = g / ncb;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (g == 0 && tid == 0) *err = 0;   // this call's error word (only the tail sets bits)
+  const int kstep0 = (kr * 4 + wave) * steps_per_wave;
+  // fragment (column block cb, k-step kstep0 + u) is 1 KiB contiguous
+  const uint16_t* wp = W + (((size_t)cb * (K >> 4) + kstep0) * 64 + lane) * 8;
+  const uint16_t* xk = X + (size_t)kstep0 * 16;
+  uint8_t* xl = xstage[wave];
 
   f32x16 acc[NRB];
 #pragma unroll
@@ -65,21 +180,24 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
     for (int r = 0; r < 16; ++r) acc[rb][r] = 0.f;
 
   int s = 0;
-  for (; s + 16 <= steps_per_wave; s += 16) gemv_run<16, NRB>(wp, xp, s, acc);
-  if (s < steps_per_wave) gemv_run<8, NRB>(wp, xp, s, acc);
+  for (; s + 16 <= steps_per_wave; s += 16) gemv_run<16, NRB>(wp, xk, K, B, s, xl, acc);
+  if (s < steps_per_wave) gemv_run<8, NRB>(wp, xk, K, B, s, xl, acc);
+  float* red = reinterpret_cast<float*>(xl);            // [NRB * 16][64] of this wave
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][rb * 16 + r][lane] = acc[rb][r];
+    for (int r = 0; r < 16; ++r) red[(rb * 16 + r) * 64 + lane] = acc[rb][r];
   __syncthreads();
   // fixed-order sum of the 4 waves; element (reg, lane) -> (row, column)
   for (int e = tid; e < NRB * 16 * 64; e += GV_THREADS) {
     const int reg = e >> 6, ln = e & 63;
-    const float v = red[0][reg][ln] + red[1][reg][ln] + red[2][reg][ln] + red[3][reg][ln];
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v += reinterpret_cast<const float*>(xstage[w])[reg * 64 + ln];
     const int rb = reg >> 4, r = reg & 15;
     const int row = rb * 32 + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-    const int col = blockIdx.x * 32 + (ln & 31);
-    if (row < B) partial[((size_t)blockIdx.y * B + row) * N + col] = v;
+    const int col = cb * 32 + (ln & 31);
+    if (row < B) partial[((size_t)kr * B + row) * N + col] = v;
   }
 }
 
@@ -88,15 +206,16 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
 //  1. the token's kv and score of channel c in every channel set: the K-range
 //     partials summed in a fixed order, Ape added to the score of position
 //     s = start_pos[b];
-//  2. if the token completes window w = (s+1)/r - 1: pool the window's slots
-//     ([PyPTO] 压缩窗口与状态更新; [CANN] 计算公式 steps 3-5) - the token
-//     itself from step 1, earlier positions from the state ring, negative
-//     positions as padding - then RMSNorm, RoPE on the last 64 channels and
-//     the optional Hadamard product, stored to output row o_b; otherwise
-//     output row o_b is +0 ([PyPTO] 返回值说明);
+//  2. if the token completes a window: merge the token's slot into the
+//     pre-pooled statistics of the window's other slots and take the pooled
+//     value ([PyPTO] 压缩窗口与状态更新; [CANN] 计算公式 steps 3-5), then
+//     RMSNorm, RoPE on the last 64 channels and the optional Hadamard
+//     product, stored to output row o_b; otherwise row o_b is +0 ([PyPTO]
+//     返回值说明);
 //  3. store the token's kv / score into ring slot s mod (coff*r) unless a
-//     C128A window just closed (no later window pools it).  That slot is never
-//     one the window reads, so reads and the write do not race.
+//     C128A window just closed (no later window pools it).  The main kernel
+//     has finished every read of the ring before this kernel starts.
+// Output rows: o_b = number of active requests before b (one ballot, B <= 64).
 // Workgroup B zero-fills the rows after the last request's.
 // ---------------------------------------------------------------------------
 constexpr int TL_THREADS = 512;
@@ -107,46 +226,33 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
     const int32_t* __restrict__ start_pos, const float* __restrict__ ape,
     float* __restrict__ kv_state, float* __restrict__ score_state,
     const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
+    const float* __restrict__ pp, const int32_t* __restrict__ ppflag,
     const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ cosv,
     const uint16_t* __restrict__ sinv, const uint16_t* __restrict__ had, uint16_t* __restrict__ out,
     int out_rows, uint32_t* __restrict__ err) {
+  constexpr int NSPLIT = dec_split<R>();
   __shared__ float red[TL_THREADS / 64];
   __shared__ float yv[512];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int D = cf.D, cD = COFF * D;
 
-  // block-wide sum (every thread of the workgroup must call it)
-  auto block_sum = [&](float v) -> float {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    __syncthreads();
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    float t = 0.f;
-#pragma unroll
-    for (int q = 0; q < TL_THREADS / 64; ++q) t += red[q];
-    return t;
-  };
-  // output rows used by requests [0, upto): each carries at most one token
-  auto rows_before = [&](int upto) -> int {
-    if (!seqused) return upto;
-    float cnt = 0.f;
-    for (int j = tid; j < upto; j += TL_THREADS) cnt += (seqused[j] == 1) ? 1.f : 0.f;
-    return int(block_sum(cnt));
-  };
+  // active requests (one token each) as a 64-bit mask, identical in every wave
+  const bool act = lane < B && (seqused ? seqused[lane] == 1 : true);
+  const unsigned long long amask = __ballot(act);
+  const int total = __popcll(amask);
 
-  if (blockIdx.x == B) {                         // rows after the last request's
-    const int total = rows_before(B);
+  if ((int)blockIdx.x == B) {                    // rows after the last request's
     if (total > out_rows && tid == 0) set_error(err, CMP_DEVERR_OUT_ROWS);
     for (long i = (long)total * D + tid; i < (long)out_rows * D; i += TL_THREADS) out[i] = 0;
     return;
   }
   const int b = blockIdx.x;
+  const int o = __popcll(amask & ((1ull << b) - 1ull));
   int n = seqused ? seqused[b] : 1;
   int s = start_pos ? start_pos[b] : 0;
   uint32_t bad = 0;
   if (n < 0 || n > 1) { bad |= CMP_DEVERR_SEQLEN; n = 0; }
   if (s < 0 || s == 0x7fffffff) { bad |= CMP_DEVERR_START_POS; n = 0; s = 0; }
-  const int o = rows_before(b);
   if (bad && tid == 0) set_error(err, bad);
   if (n == 0) return;
   if (o >= out_rows) {
@@ -158,72 +264,107 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
   const int c = tid;
   const bool own = c < D;
 
-  // 1. the token's projected values of channel c
+  // 1. the token's projected values of channel c, and (completing) the
+  //    pre-pooled statistics: every load before the first use
   float kvc[COFF], zc[COFF];
+  float pm[NSPLIT], pl[NSPLIT], px[NSPLIT];
 #pragma unroll
   for (int cs = 0; cs < COFF; ++cs) { kvc[cs] = 0.f; zc[cs] = 0.f; }
   if (own) {
     const float* pb = partial + (size_t)b * cf.N;
     const size_t kstride = (size_t)B * cf.N;
+    // all K ranges' loads in flight at once (KS <= DEC_MAX_KSPLIT), summed
+    // in K order
+    float pk[COFF][DEC_MAX_KSPLIT], pz[COFF][DEC_MAX_KSPLIT];
 #pragma unroll
     for (int cs = 0; cs < COFF; ++cs) {
       const int ck = packed_col(0, cs, c, COFF), cz = packed_col(1, cs, c, COFF);
-      for (int ks = 0; ks < KS; ++ks) {
-        kvc[cs] += pb[ks * kstride + ck];
-        zc[cs] += pb[ks * kstride + cz];
+#pragma unroll
+      for (int ks = 0; ks < DEC_MAX_KSPLIT; ++ks) {
+        pk[cs][ks] = ks < KS ? pb[ks * kstride + ck] : 0.f;
+        pz[cs][ks] = ks < KS ? pb[ks * kstride + cz] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int cs = 0; cs < COFF; ++cs) {
+#pragma unroll
+      for (int ks = 0; ks < DEC_MAX_KSPLIT; ++ks) {
+        kvc[cs] += pk[cs][ks];
+        zc[cs] += pz[cs][ks];
       }
       zc[cs] += ape[(long)(s % R) * cD + cs * D + c];
     }
+    if (completing) {
+#pragma unroll
+      for (int q = 0; q < NSPLIT; ++q) {
+        const float* st = pp + ((size_t)(b * NSPLIT + q) * 3) * D + c;
+        pm[q] = st[0];
+        pl[q] = st[D];
+        px[q] = st[2 * D];
+      }
+    }
   }
-  uint32_t tbad = 0;
+  if (completing && tid < NSPLIT) {
+    const int32_t f = ppflag[b * NSPLIT + tid];
+    if (f) set_error(err, (uint32_t)f);
+  }
+  // loads the later steps need, issued with the ones above: norm weight,
+  // this channel's cos / sin columns, the token's state rows
+  const int rope0 = D - cf.rope;
+  const bool rope_lane = own && c >= rope0;
+  const float g = own ? bf2f(gamma[c]) : 0.f;
+  float rc = 0.f, rsn = 0.f;
+  if (completing && rope_lane) {
+    const int col = ((c - rope0) >> 1) + ((c & 1) ? cf.rope / 2 : 0);
+    rc = bf2f(cosv[(size_t)o * cf.rope + col]);
+    rsn = bf2f(sinv[(size_t)o * cf.rope + col]);
+  }
+  const int lo = max(s, R * (e / R) - (COFF - 1) * R);
+  long rk = 0, rs = 0;
+  const bool store_row = lo <= s;
+  const bool rows_ok = store_row && state_row(cf, kv_tab, b, s, &rk) && state_row(cf, st_tab, b, s, &rs);
 
   if (completing) {
-    // 2. pooling of channel c over the window's slots
+    // 2. pooled value of channel c: the token is the window's last slot
+    //    (second channel set for C4A)
     float pooled = 0.f;
     if (own) {
-      const int w = e / R - 1;
-      float m = -INFINITY, l = 0.f, a = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < COFF * R; ++j) {
-        const int cs = (COFF == 2) ? (j >= R) : 0;
-        const int p = (COFF == 2) ? (w - 1 + cs) * R + (j - cs * R) : w * R + j;
-        if (p < 0) continue;
-        float kv, z;
-        if (p == s) {
-          kv = kvc[cs];
-          z = zc[cs];
-        } else {
-          long rk, rs;
-          if (!state_row(cf, kv_tab, b, p, &rk) || !state_row(cf, st_tab, b, p, &rs)) {
-            tbad |= CMP_DEVERR_TABLE;
-            continue;
-          }
-          kv = kv_state[rk * cD + cs * D + c];
-          z = score_state[rs * cD + cs * D + c];
+      const float zt = zc[COFF - 1], kt = kvc[COFF - 1];
+      float m = zt;
+#pragma unroll
+      for (int q = 0; q < NSPLIT; ++q) m = fmaxf(m, pm[q]);
+      float l = 0.f, x = 0.f;
+      if (m != -INFINITY) {
+        if (zt != -INFINITY) {
+          const float et = __expf(zt - m);
+          l = et;
+          x = et * kt;
         }
-        if (z == -INFINITY) continue;
-        const float mn = fmaxf(m, z);
-        const float sc = __expf(m - mn), pe = __expf(z - mn);
-        l = l * sc + pe;
-        a = a * sc + pe * kv;
-        m = mn;
+#pragma unroll
+        for (int q = 0; q < NSPLIT; ++q) {
+          if (pl[q] > 0.f) {
+            const float sc = __expf(pm[q] - m);
+            l = fmaf(pl[q], sc, l);
+            x = fmaf(px[q], sc, x);
+          }
+        }
       }
-      pooled = l > 0.f ? a / l : 0.f;
+      pooled = l > 0.f ? x / l : 0.f;
     }
-    // RMSNorm over the D channels
-    const float ss = block_sum(own ? pooled * pooled : 0.f);
+    // RMSNorm over the D channels (block-wide sum)
+    float v = own ? pooled * pooled : 0.f;
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < TL_THREADS / 64; ++q) ss += red[q];
     const float inv = rsqrtf(ss / float(D) + kRmsEps);
-    float y = own ? pooled * inv * bf2f(gamma[c < D ? c : 0]) : 0.f;
-    // RoPE: pair (2i, 2i+1) of the trailing rope slice, partner via lane ^ 1
+    float y = own ? pooled * inv * g : 0.f;
+    // RoPE: pair (2i, 2i+1) of the trailing rope slice, partner via lane ^ 1;
+    // the even element takes cos/sin column i, the odd one column 32 + i
     const float partner = __shfl_xor(y, 1, 64);
-    const int rope0 = D - cf.rope;
-    if (own && c >= rope0) {
-      const int pr = (c - rope0) >> 1, half = cf.rope / 2;
-      const uint16_t* cr = cosv + (size_t)o * cf.rope;
-      const uint16_t* sr = sinv + (size_t)o * cf.rope;
-      y = (c & 1) == 0 ? y * bf2f(cr[pr]) - partner * bf2f(sr[pr])
-                       : y * bf2f(cr[half + pr]) + partner * bf2f(sr[half + pr]);
-    }
+    if (rope_lane) y = (c & 1) == 0 ? y * rc - partner * rsn : y * rc + partner * rsn;
     uint16_t* orow = out + (size_t)o * D;
     if (!cf.rotate) {
       if (own) orow[c] = f2bf(y);
@@ -242,12 +383,9 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
   }
 
   // 3. the token's state row
-  const int lo = max(s, R * (e / R) - (COFF - 1) * R);
-  if (own && lo <= s) {
-    long rk, rs;
-    const bool okk = state_row(cf, kv_tab, b, s, &rk);
-    const bool oks = state_row(cf, st_tab, b, s, &rs);
-    if (okk && oks) {
+  uint32_t tbad = 0;
+  if (own && store_row) {
+    if (rows_ok) {
 #pragma unroll
       for (int cs = 0; cs < COFF; ++cs) {
         kv_state[rk * cD + cs * D + c] = kvc[cs];

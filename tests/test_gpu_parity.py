@@ -291,3 +291,44 @@ def test_prefill_equals_token_by_token_decode(harness):
             off = q % w["block_size"]
             assert np.allclose(kvp[kb, off], kvd[kb, off], rtol=1e-3, atol=1e-3)
             assert np.allclose(scp[sb, off], scd[sb, off], rtol=1e-3, atol=1e-3)
+
+
+# --------------------------------------------------------------------------
+# HIP graph capture: no host sync, allocation or memset inside a call, so a
+# captured call replays to the eager result.  Every replay is checked, with
+# eager work and synchronisation between replays.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name,entry", [("decode_c4a_all", "decode"),
+                                        ("decode_c128a_all", "decode"),
+                                        ("c4li_small", "prefill")])
+def test_graph_replay_matches_eager(harness, name, entry):
+    _announce(f"graph replay {name} {entry}")
+    w = workloads.build_named(name)
+    case = harness.DeviceCase(w)
+    call = getattr(case, entry)
+    call()
+    torch.cuda.synchronize()
+    ref_out = case.out_bits().copy()
+    ref_kv, ref_sc = case.states()
+    case.reset_state()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                                    # warm-up on the capture stream's side
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        case.reset_state()                        # eager work between replays
+        case.out.fill_(0x7F7F)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(case.out_bits(), ref_out), f"replay {rep}: output differs"
+        kv, sc = case.states()
+        assert np.array_equal(kv.view(np.uint32), ref_kv.view(np.uint32)), f"replay {rep}: kv"
+        assert np.array_equal(sc.view(np.uint32), ref_sc.view(np.uint32)), f"replay {rep}: score"
+    assert case.device_error() == 0

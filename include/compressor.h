@@ -60,9 +60,11 @@ typedef enum {
 /*
  * Static shape of a Compressor layer.
  *
- * ratio         r, tokens per compressed row: 4 or 128 ([CANN] 约束说明 lists
- *               the C4A / C4Li / C128A combinations).  coff, the number of
- *               channel sets, is 2 for ratio 4 and 1 otherwise ([PyPTO] 参数说明).
+ * ratio         r, tokens per compressed row: 2, 4, 8, 16, 32, 64 or 128
+ *               ([CANN] 约束说明, which also names the C4A / C4Li / C128A
+ *               combinations); any other value is CMP_ERR_UNSUPPORTED.  coff,
+ *               the number of channel sets, is 2 for ratio 4 and 1 otherwise
+ *               ([PyPTO] 参数说明).
  * head_dim      D: 128 or 512.
  * hidden        H: multiple of 512 in [1024, 10240].
  * rope_head_dim 64 (the only supported value, [PyPTO] 参数说明).

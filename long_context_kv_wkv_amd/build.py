@@ -22,7 +22,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     tmp = OUT + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-shared", "-fPIC",
            "-I", os.path.join(ROOT, "include"),
            # no packed fp32 instructions in device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

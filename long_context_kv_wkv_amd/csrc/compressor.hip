@@ -72,7 +72,8 @@ int launch(const char* name, hipStream_t stream, F&& fn) {
 // ---------------------------------------------------------------------------
 int check_shape(const compressor_shape* sh, Cfg* cf) {
   if (!sh) return CMP_ERR_NULLPTR;
-  if (sh->ratio != 4 && sh->ratio != 128) return CMP_ERR_UNSUPPORTED;
+  // cmp_ratio 2, 4, 8, 16, 32, 64 or 128 ([CANN] 约束说明)
+  if (sh->ratio < 2 || sh->ratio > 128 || (sh->ratio & (sh->ratio - 1))) return CMP_ERR_UNSUPPORTED;
   if (sh->head_dim != 128 && sh->head_dim != 512) return CMP_ERR_UNSUPPORTED;
   if (sh->hidden < 1024 || sh->hidden > 10240 || sh->hidden % 512) return CMP_ERR_INVALID;
   if (sh->rope_head_dim != 64) return CMP_ERR_UNSUPPORTED;
@@ -92,6 +93,27 @@ int check_shape(const compressor_shape* sh, Cfg* cf) {
   cf->nblocks = sh->num_blocks;
   cf->stride = sh->table_stride;
   return CMP_OK;
+}
+
+// The kernel of each ratio (coff = 2 only at ratio 4).
+template <int R>
+constexpr int coff_of() { return R == 4 ? 2 : 1; }
+template <int R>
+const void* gemm_kernel_of() {
+  return reinterpret_cast<const void*>(gemm_pool_kernel<R, coff_of<R>()>);
+}
+// Calls f.template operator()<R>() for the compile-time ratio equal to r.
+template <typename F>
+void with_ratio(int r, F&& f) {
+  switch (r) {
+    case 2: f.template operator()<2>(); break;
+    case 4: f.template operator()<4>(); break;
+    case 8: f.template operator()<8>(); break;
+    case 16: f.template operator()<16>(); break;
+    case 32: f.template operator()<32>(); break;
+    case 64: f.template operator()<64>(); break;
+    default: f.template operator()<128>(); break;
+  }
 }
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -144,7 +166,7 @@ struct DecodeLayout {
 DecodeLayout decode_layout(const Cfg& cf, int B) {
   DecodeLayout L;
   L.ks = decode_ksplit(cf);
-  L.split = cf.ratio == 4 ? dec_split<4>() : dec_split<128>();
+  with_ratio(cf.ratio, [&]<int R>() { L.split = dec_split<R>(); });
   size_t o = 0;
   L.err = o;       o += 256;
   L.partial = o;   o = align256(o + (size_t)L.ks * B * cf.N * 4);
@@ -180,13 +202,14 @@ int ensure_lds_limits() {
   static std::once_flag flag;
   static hipError_t status = hipSuccess;
   std::call_once(flag, [] {
-    hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pool_kernel<4, 2>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        GM_LDS_BYTES);
-    hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pool_kernel<128, 1>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        GM_LDS_BYTES);
-    if (e1 == hipSuccess) e1 = e0;
+    hipError_t e1 = hipSuccess;
+    for (int r = 2; r <= 128; r *= 2)
+      with_ratio(r, [&]<int R>() {
+        const hipError_t e = hipFuncSetAttribute(gemm_kernel_of<R>(),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 GM_LDS_BYTES);
+        if (e1 == hipSuccess) e1 = e;
+      });
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(post_kernel<8>),
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         POST_ROWS * 512 * 2);
@@ -321,7 +344,8 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
     const long nwg = (long)prefill_max_tiles(cf, T, B) * tiles_n;
     const int grid = int((nwg + 7) / 8 * 8);
     CMP_TRY(launch("gemm", st, [&] {
-      auto kern = cf.ratio == 4 ? gemm_pool_kernel<4, 2> : gemm_pool_kernel<128, 1>;
+      decltype(&gemm_pool_kernel<4, 2>) kern = nullptr;
+      with_ratio(cf.ratio, [&]<int R>() { kern = gemm_pool_kernel<R, coff_of<R>()>; });
       hipLaunchKernelGGL(kern, dim3(grid), dim3(GM_THREADS), GM_LDS_BYTES, st, cf,
                          static_cast<const uint16_t*>(a->x),
                          static_cast<const uint16_t*>(a->w_packed), T, B, plan, tiles, a->ape,
@@ -369,14 +393,17 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
   CMP_TRY(launch("decode_main", st, [&] {
     const uint16_t* X = static_cast<const uint16_t*>(a->x);
     const uint16_t* W = static_cast<const uint16_t*>(a->w_packed);
-    auto kern = cf.ratio == 4 ? (B <= 32 ? decode_main_kernel<1, 4, 2> : decode_main_kernel<2, 4, 2>)
-                              : (B <= 32 ? decode_main_kernel<1, 128, 1> : decode_main_kernel<2, 128, 1>);
+    decltype(&decode_main_kernel<1, 4, 2>) kern = nullptr;
+    with_ratio(cf.ratio, [&]<int R>() {
+      kern = B <= 32 ? decode_main_kernel<1, R, coff_of<R>()> : decode_main_kernel<2, R, coff_of<R>()>;
+    });
     hipLaunchKernelGGL(kern, gg, dim3(GV_THREADS), 0, st, cf, X, W, partial, B, steps, a->seqused,
                        a->start_pos, a->kv_state, a->score_state, kvt, a->state_block_table, pp,
                        ppflag, err);
   }));
   return launch("decode_tail", st, [&] {
-    auto tail = cf.ratio == 4 ? decode_tail_kernel<4, 2> : decode_tail_kernel<128, 1>;
+    decltype(&decode_tail_kernel<4, 2>) tail = nullptr;
+    with_ratio(cf.ratio, [&]<int R>() { tail = decode_tail_kernel<R, coff_of<R>()>; });
     hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, L.ks, B,
                        a->seqused, a->start_pos, a->ape, a->kv_state, a->score_state, kvt,
                        a->state_block_table, pp, ppflag,

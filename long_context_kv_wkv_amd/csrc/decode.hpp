@@ -69,13 +69,11 @@ __device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp,
 // the token itself ([PyPTO] 压缩窗口与状态更新; [CANN] 计算公式 steps 3-5):
 // per channel the softmax statistics (max m, sum l, weighted sum x) of those
 // slots.  None of them depends on this call's projection, so they run while
-// the GEMV streams the panel.  A C128A window (127 ring rows) is split over
-// DEC_SPLIT_C128 workgroups of 16 slots; a C4A window (7 ring rows) takes one.
-// Every load of a workgroup is issued before its first exponential.
-constexpr int DEC_SPLIT_C128 = 8;
+// the GEMV streams the panel.  A window of more than 16 slots is split over
+// workgroups of 16 slots (C128A: 8 of them); smaller windows take one.
 constexpr int DEC_MAX_KSPLIT = 20;           // K ranges of the GEMV (H / 512 at most)
 template <int R>
-constexpr int dec_split() { return R == 4 ? 1 : DEC_SPLIT_C128; }
+constexpr int dec_split() { return R <= 16 ? 1 : R / 16; }
 
 template <int R, int COFF>
 __device__ __forceinline__ void prepool_block(const Cfg& cf, int b, int sp,
@@ -213,7 +211,7 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
 //     product, stored to output row o_b; otherwise row o_b is +0 ([PyPTO]
 //     返回值说明);
 //  3. store the token's kv / score into ring slot s mod (coff*r) unless a
-//     C128A window just closed (no later window pools it).  The main kernel
+//     coff = 1 window just closed (no later window pools it).  The main kernel
 //     has finished every read of the ring before this kernel starts.
 // Output rows: o_b = number of active requests before b (one ballot, B <= 64).
 // Workgroup B zero-fills the rows after the last request's.

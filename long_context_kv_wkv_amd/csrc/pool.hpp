@@ -141,6 +141,160 @@ __device__ __forceinline__ void store_state(const Cfg& cf, float* __restrict__ k
   }
 }
 
+// ---------------------------------------------------------------------------
+// coff = 1 epilogue (ratios 2, 8, 16, ..., 128): the windows of a row-wave's
+// 128 rows.  Register r of block i holds wave row 32 i + 8 (r / 4) + 4 h + r % 4
+// (h = lane / 32), so a window of R <= 4 rows lies in one lane (R = 4: one
+// run of 4 rows, R = 2: half a run), and a window of R >= 8 rows is split
+// between the two lane halves: each half takes the statistics of its rows
+// (max first, then the exponentials), one cross-half swap merges them, and
+// the low half writes channel c0, the high half c1.  FAST: every row is a
+// token of this call and every window complete (no per-row tests).
+// ---------------------------------------------------------------------------
+struct EpiCtx {
+  const Cfg& cf;
+  int base;            // position of wave row 0 (a multiple of R)
+  int s, e, live_lo, first;
+  const float* stg;    // staged ring rows of positions [first, s)
+  const float* ape;
+  int c0, c1, h;
+  int orow0;           // output row of the wave's first window, if complete
+  int wfirst, wend, wg0;
+  int out_rows;
+  float* pooled;
+};
+
+// value of channel c of (kv or score) at wave row jr: accumulator, Ape, or
+// the staged row for positions before the call; false if no token there
+template <int R, bool FAST>
+__device__ __forceinline__ bool epi_value(const EpiCtx& t, float a_kv, float a_z, int jr, int c,
+                                          float& kv, float& z) {
+  const int cD = t.cf.D;
+  if (FAST) {
+    kv = a_kv;
+    z = a_z + t.ape[(jr % R) * cD + c];
+    return true;
+  }
+  const int p = t.base + jr;
+  if (p >= t.e) return false;
+  if (p < t.s) {
+    const float* row = t.stg + (size_t)(p - t.first) * 2 * cD;
+    kv = row[c];
+    z = row[cD + c];
+  } else {
+    kv = a_kv;
+    z = a_z + t.ape[(jr % R) * cD + c];
+  }
+  return z != -INFINITY;
+}
+
+// pooled value of one window from its statistics, to its output row
+__device__ __forceinline__ void epi_store(const EpiCtx& t, int wl, int c, const Soft& st) {
+  const int wg = t.wg0 + wl;
+  if (wg < t.wfirst || wg >= t.wend) return;
+  const int row = t.orow0 + wl;
+  if (row < t.out_rows) t.pooled[(size_t)row * t.cf.D + c] = st.l > 0.f ? st.x / st.l : 0.f;
+}
+
+template <int R, bool FAST>
+__device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&acc)[4][4]) {
+  const int h = t.h;
+  if constexpr (R <= 4) {
+    // windows inside one lane: R = 4 -> (i, run), R = 2 -> (i, run, pair)
+    constexpr int PER_RUN = 4 / R;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+        for (int pw = 0; pw < PER_RUN; ++pw) {
+          float kv[2][R], z[2][R];
+          bool ok[2][R];
+#pragma unroll
+          for (int q = 0; q < R; ++q) {
+            const int r = 4 * rg + pw * R + q;
+            const int jr = 32 * i + 8 * rg + 4 * h + pw * R + q;
+            ok[0][q] = epi_value<R, FAST>(t, acc[i][0][r], acc[i][1][r], jr, t.c0, kv[0][q], z[0][q]);
+            ok[1][q] = epi_value<R, FAST>(t, acc[i][2][r], acc[i][3][r], jr, t.c1, kv[1][q], z[1][q]);
+          }
+          const int wl = (32 * i + 8 * rg + 4 * h + pw * R) / R;   // window in the wave
+#pragma unroll
+          for (int ch = 0; ch < 2; ++ch) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int q = 0; q < R; ++q) if (ok[ch][q]) m = fmaxf(m, z[ch][q]);
+            Soft st{m, 0.f, 0.f};
+            if (m != -INFINITY) {
+#pragma unroll
+              for (int q = 0; q < R; ++q) {
+                if (!ok[ch][q]) continue;
+                const float pe = __builtin_amdgcn_exp2f((z[ch][q] - m) * kLog2e);
+                st.l += pe;
+                st.x = fmaf(pe, kv[ch][q], st.x);
+              }
+            }
+            epi_store(t, wl, ch ? t.c1 : t.c0, st);
+          }
+        }
+  } else {
+    // R >= 8: wave window w holds blocks i and runs rg with
+    // (32 i + 8 rg) / R == w, in both lane halves
+    constexpr int NW = 128 / R;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      Soft st[2];
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if ((32 * i + 8 * (r >> 2)) / R != w) continue;
+            const int jr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+            float kv, z;
+            if (epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r], jr, ch ? t.c1 : t.c0, kv, z))
+              m = fmaxf(m, z);
+          }
+        st[ch] = Soft{m, 0.f, 0.f};
+        if (m != -INFINITY) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              if ((32 * i + 8 * (r >> 2)) / R != w) continue;
+              const int jr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+              float kv, z;
+              if (epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r], jr, ch ? t.c1 : t.c0, kv, z)) {
+                const float pe = __builtin_amdgcn_exp2f((z - m) * kLog2e);
+                st[ch].l += pe;
+                st[ch].x = fmaf(pe, kv, st[ch].x);
+              }
+            }
+        }
+      }
+      // the low half needs the high half's c0 rows, the high half the low
+      // half's c1 rows
+      const Soft mine = h ? st[1] : st[0];
+      const Soft other{cross_half(st[0].m, st[1].m, h), cross_half(st[0].l, st[1].l, h),
+                       cross_half(st[0].x, st[1].x, h)};
+      const float mn = fmaxf(mine.m, other.m);
+      Soft tot{mn, 0.f, 0.f};
+      if (mine.l > 0.f) {
+        const float sc = __builtin_amdgcn_exp2f((mine.m - mn) * kLog2e);
+        tot.l += mine.l * sc;
+        tot.x += mine.x * sc;
+      }
+      if (other.l > 0.f) {
+        const float sc = __builtin_amdgcn_exp2f((other.m - mn) * kLog2e);
+        tot.l += other.l * sc;
+        tot.x += other.x * sc;
+      }
+      epi_store(t, w, h ? t.c1 : t.c0, tot);
+    }
+  }
+}
+
 template <int R, int COFF>
 __global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
     Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int T, int B,
@@ -355,64 +509,39 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
       }
     }
   } else {
-    // ---- ratio 128: row-wave wm holds window W0 + wm; lane (wn, lrow)
-    // owns channels c0 (blocks 0: kv, 1: score) and c1 (blocks 2, 3) ----
+    // ---- coff = 1: lane (wn, lrow) owns channels c0 (blocks 0: kv,
+    // 1: score) and c1 (blocks 2, 3) ----
     const int g = (n0 + wn * 128) >> 7;
     const int c0 = g * 64 + lrow, c1 = c0 + 32;
-    Soft s0{-INFINITY, 0.f, 0.f}, s1{-INFINITY, 0.f, 0.f};
+    EpiCtx ctx{cf, P0 + 128 * wm, s, e, live_lo, rec[PL_FIRST], stg, ape, c0, c1, h,
+               o + (P0 + 128 * wm) / R - wfirst, wfirst, wend, (P0 + 128 * wm) / R,
+               out_rows, pooled};
+    if (P0 >= s && P0 + GM_BM <= live_lo) {
+      epilogue_coff1<R, true>(ctx, acc);
+    } else {
+      epilogue_coff1<R, false>(ctx, acc);
+      // state rows that stay live (only a request's last tile has any)
+      if (P0 + 128 * wm + 127 >= live_lo && P0 + 128 * wm < e) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jw = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);   // row in the window
-        const int p = P0 + 128 * wm + jw;
-        float kv0 = acc[i][0][r], kv1 = acc[i][2][r];
-        float z0 = acc[i][1][r], z1 = acc[i][3][r];
-        const bool valid = p >= 0 && p < e;
-        if (valid && p < s) {
-          const float* row = stg + (size_t)(p - rec[PL_FIRST]) * 2 * cD;
-          kv0 = row[c0];
-          kv1 = row[c1];
-          z0 = row[cD + c0];
-          z1 = row[cD + c1];
-        } else if (valid) {
-          z0 += ape[jw * cD + c0];
-          z1 += ape[jw * cD + c1];
-        }
-        if (valid && z0 != -INFINITY) soft_add(s0, z0, kv0);
-        if (valid && z1 != -INFINITY) soft_add(s1, z1, kv1);
-      }
-    }
-    // state rows that stay live (only the request's last tile has any)
-    if (P0 + 128 * wm + 127 >= live_lo && P0 + 128 * wm < e) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jw = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-          const int p = P0 + 128 * wm + jw;
-          if (p >= live_lo && p < e) {
-            long rk, rs;
-            if (state_row(cf, kv_tab, b, p, &rk) && state_row(cf, st_tab, b, p, &rs)) {
-              kv_state[rk * cD + c0] = acc[i][0][r];
-              kv_state[rk * cD + c1] = acc[i][2][r];
-              score_state[rs * cD + c0] = acc[i][1][r] + ape[jw * cD + c0];
-              score_state[rs * cD + c1] = acc[i][3][r] + ape[jw * cD + c1];
-            } else {
-              bad |= CMP_DEVERR_TABLE;
+          for (int r = 0; r < 16; ++r) {
+            const int jr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);   // row in the wave
+            const int p = P0 + 128 * wm + jr;
+            if (p >= live_lo && p < e) {
+              long rk, rs;
+              if (state_row(cf, kv_tab, b, p, &rk) && state_row(cf, st_tab, b, p, &rs)) {
+                const int q = p % R;
+                kv_state[rk * cD + c0] = acc[i][0][r];
+                kv_state[rk * cD + c1] = acc[i][2][r];
+                score_state[rs * cD + c0] = acc[i][1][r] + ape[q * cD + c0];
+                score_state[rs * cD + c1] = acc[i][3][r] + ape[q * cD + c1];
+              } else {
+                bad |= CMP_DEVERR_TABLE;
+              }
             }
           }
         }
-      }
-    }
-    s0 = soft_merge(s0, soft_shfl_xor(s0, 32));
-    s1 = soft_merge(s1, soft_shfl_xor(s1, 32));
-    const int Wg = P0 / 128 + wm;
-    if (Wg >= wfirst && Wg < wend) {
-      const int row = o + (Wg - wfirst);
-      if (row < out_rows) {
-        const Soft t = h == 0 ? s0 : s1;
-        pooled[(size_t)row * D + (h == 0 ? c0 : c1)] = t.l > 0.f ? t.x / t.l : 0.f;
       }
     }
   }

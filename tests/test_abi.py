@@ -40,7 +40,6 @@ def test_status_strings():
 def test_workspace_sizes_and_shape_checks():
     sh = cmp.make_shape(4, 512, 7168, True, 128, 1, 1)
     n = cmp.compressor_prefill_workspace_size(sh, 131072, 1, 32768)
-    # projection rows of 2048 fp32 columns dominate
     # pooled rows, staging and split-window statistics; no projection buffer
     assert 32768 * 512 * 4 <= n < 131072 * 2048 * 4
     assert cmp.compressor_decode_workspace_size(sh, 32, 32) > 0
@@ -56,6 +55,17 @@ def test_workspace_sizes_and_shape_checks():
     with pytest.raises(cmp.CompressorError) as ei:
         cmp.compressor_decode_workspace_size(sh, 65, 65)
     assert ei.value.status == 3
+    # every listed ratio is accepted (table stride covers coff * ratio slots),
+    # nothing else
+    for r in (2, 8, 16, 32, 64, 128):
+        ok = cmp.make_shape(r, 512, 4096, False, 16, 64, -(-r // 16))
+        assert cmp.compressor_prefill_workspace_size(ok, 1000, 2, 600) > 0
+        assert cmp.compressor_decode_workspace_size(ok, 32, 32) > 0
+    for r in (1, 6, 12, 256):
+        with pytest.raises(cmp.CompressorError) as ei:
+            cmp.compressor_prefill_workspace_size(cmp.make_shape(r, 512, 4096, False, 256, 64, 1),
+                                                  64, 1, 16)
+        assert ei.value.status == 3
 
 
 def test_null_arguments_rejected_before_any_launch():

@@ -196,9 +196,10 @@ def test_c4a_pipeline_hand_worked():
 def test_uniform_scores_give_plain_mean():
     """Wgate = 0 and Ape = 0: each window's output is RMSNorm of the plain mean
     of its valid slots (C4A: the a half of the 4 previous rows and the b half
-    of the 4 current ones; window 0 only the 4 b rows; C128A the 128 rows)."""
+    of the 4 current ones; window 0 only the 4 b rows; every other ratio its
+    own r rows)."""
     rng = np.random.default_rng(4)
-    for ratio, T in ((4, 20), (128, 300)):
+    for ratio, T in ((4, 20), (128, 300), (2, 11), (16, 50)):
         coff = O.coff_of(ratio)
         D, H = 64, 16
         x = rng.standard_normal((T, H))

@@ -88,7 +88,7 @@ def random_chunks(rng, n, max_pieces):
     return list(np.diff(edges))
 
 
-@pytest.mark.parametrize("ratio", [4, 128, 8])
+@pytest.mark.parametrize("ratio", [4, 128, 8, 2])
 def test_prefill_equals_random_splits_and_token_by_token(ratio):
     rng = np.random.default_rng(100 + ratio)
     lengths = (int(rng.integers(1, 3 * ratio)), int(rng.integers(1, 3 * ratio)), 3)

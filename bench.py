@@ -25,6 +25,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+DECODE_WORKLOADS = ("decode_c4a", "decode_c128a", "decode_c4a_all", "decode_c128a_all",
+                    "decode_c4a_mtp2")
 
 
 def kernel_source_sha(*names):
@@ -84,22 +86,24 @@ def bench_prefill(steps, warmup):
 
 
 def decode_bytes(w):
-    """Algorithmic HBM bytes of one decode step: the panel, x, the ring rows a
-    completing window reads (kv and score of its channel set), the state rows
-    written, the output rows."""
+    """Algorithmic HBM bytes of one decode step: the panel, x, the ring rows
+    the completed windows read (kv and score of their channel set), the state
+    rows written, the output rows."""
     r, coff, D, H, B = w["ratio"], w["coff"], w["head_dim"], w["hidden"], w["batch"]
     N = 2 * coff * D
-    total = N * H * 2 + B * H * 2 + w["out_rows"] * D * 2
-    seq = w["seqused"] if w["seqused"] is not None else np.ones(B, np.int32)
+    total = N * H * 2 + w["T"] * H * 2 + w["out_rows"] * D * 2
+    slots = np.diff(w["cu_seqlens"]).astype(np.int64)
+    seq = w["seqused"] if w["seqused"] is not None else slots
     for b in range(B):
-        if seq[b] != 1:
+        n = int(seq[b])
+        if n == 0:
             continue
-        s = int(w["start_pos"][b])
-        e = s + 1
-        if e % r == 0:
-            total += (coff * r - 1) * D * 8          # the window's other slots, kv + score
-        if max(s, r * (e // r) - (coff - 1) * r) <= s:
-            total += coff * D * 8                    # the token's state row
+        s = int(w["start_pos"][b]) if w["start_pos"] is not None else 0
+        e = s + n
+        for wi in range(s // r, e // r):
+            lo = (wi - (coff - 1)) * r
+            total += sum(1 for p in range(lo, (wi + 1) * r) if 0 <= p < s) * D * 8
+        total += (e - max(s, r * (e // r) - (coff - 1) * r)) * coff * D * 8
     return total
 
 
@@ -118,9 +122,12 @@ def bench_decode(name, steps, warmup, copies=12):
     kvs = [case.kv_state] + [case.kv_state.clone() for _ in range(copies - 1)]
     scs = [case.score_state] + [case.score_state.clone() for _ in range(copies - 1)]
 
+    cu = case.cu_seqlens if w["T"] != w["batch"] else None
+
     def run(i):
         j = i % copies
-        case.decode(w_packed=panels[j], x=xs[j], kv_state=kvs[j], score_state=scs[j])
+        case.decode(w_packed=panels[j], x=xs[j], kv_state=kvs[j], score_state=scs[j],
+                    cu_seqlens=cu)
 
     for i in range(warmup):
         run(i)
@@ -328,7 +335,7 @@ def main():
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
         return
     if a.decode_only:
-        for name in ("decode_c4a", "decode_c128a", "decode_c4a_all", "decode_c128a_all"):
+        for name in DECODE_WORKLOADS:
             print(name, json.dumps(bench_decode(name, a.decode_steps, 5)), flush=True)
         return
     pre = bench_prefill(a.steps, a.warmup)
@@ -360,7 +367,7 @@ def main():
     }
     if not a.no_decode:
         dec = {}
-        for name in ("decode_c4a", "decode_c128a", "decode_c4a_all", "decode_c128a_all"):
+        for name in DECODE_WORKLOADS:
             d = bench_decode(name, a.decode_steps, 20)
             dec[name] = {"us_per_step": d["us_per_step"],
                          "us_per_step_eager": d["us_per_step_eager"],

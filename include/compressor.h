@@ -54,7 +54,8 @@ typedef enum {
 /* Bits of the device error word. */
 #define CMP_DEVERR_TABLE 1u      /* block-table entry outside [0, num_blocks) */
 #define CMP_DEVERR_START_POS 2u  /* start_pos < 0: request treated as empty */
-#define CMP_DEVERR_SEQLEN 4u     /* cu_seqlens not monotone / beyond T, or seqused outside [0, slot] */
+#define CMP_DEVERR_SEQLEN 4u     /* cu_seqlens not monotone / beyond T, seqused outside [0, slot], or
+                                    more than 4 tokens in a decode request */
 #define CMP_DEVERR_OUT_ROWS 8u   /* sum over requests of ceil(n_b / ratio) > out_rows */
 
 /*
@@ -158,7 +159,8 @@ typedef struct {
 int compressor_prefill_workspace_size(const compressor_shape* shape, int32_t T, int32_t batch,
                                       int32_t out_rows, size_t* bytes);
 
-/* Workspace bytes a decode call with `batch` requests needs (host only). */
+/* Workspace bytes a decode call with `batch` requests (and any T <= 64)
+ * needs (host only). */
 int compressor_decode_workspace_size(const compressor_shape* shape, int32_t batch,
                                      int32_t out_rows, size_t* bytes);
 
@@ -188,9 +190,15 @@ int compressor_state_reset(const compressor_shape* shape, float* kv_state, float
  * write-back described at compressor_args. */
 int compressor_prefill(const compressor_shape* shape, const compressor_args* args, void* stream);
 
-/* The same operator for one token per request ([Triton] 性能优化: decode has
- * one token per request and different scheduling).  x is [batch, H];
- * cu_seqlens must be NULL; seqused, if given, is 0 or 1 per request. */
+/* The same operator for decode steps of at most 4 tokens per request
+ * ([Triton] 性能优化: decode has few tokens per request and different
+ * scheduling; [PyPTO] 参数说明: S up to 4 for multi-token prediction).
+ * x is [T, H] with T <= 64 packed rows and batch <= 64
+ * (CMP_ERR_UNSUPPORTED otherwise).  cu_seqlens NULL: one row per request
+ * (T == batch); else request b owns rows [cu[b], cu[b+1]).  n_b = seqused[b]
+ * (or the slot length) must be <= 4: a larger value sets CMP_DEVERR_SEQLEN
+ * and the request is treated as empty.  Output rows, state semantics and
+ * errors are those of compressor_prefill. */
 int compressor_decode(const compressor_shape* shape, const compressor_args* args, void* stream);
 
 /* Synchronise `stream`, then read the device error word (CMP_DEVERR_* bits)

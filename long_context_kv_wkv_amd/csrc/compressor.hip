@@ -4,6 +4,7 @@
 
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -158,6 +159,7 @@ int decode_ksplit(const Cfg& cf) {
 }
 
 constexpr int kDecodeMaxBatch = 64;
+constexpr int kDecodeMaxRows = 64;       // packed x rows of a decode call
 
 struct DecodeLayout {
   size_t err, partial, pp, ppflag, total;
@@ -169,9 +171,9 @@ DecodeLayout decode_layout(const Cfg& cf, int B) {
   with_ratio(cf.ratio, [&]<int R>() { L.split = dec_split<R>(); });
   size_t o = 0;
   L.err = o;       o += 256;
-  L.partial = o;   o = align256(o + (size_t)L.ks * B * cf.N * 4);
-  L.pp = o;        o = align256(o + (size_t)B * L.split * 3 * cf.D * 4);
-  L.ppflag = o;    o = align256(o + (size_t)B * L.split * 4);
+  L.partial = o;   o = align256(o + (size_t)L.ks * kDecodeMaxRows * cf.N * 4);
+  L.pp = o;        o = align256(o + (size_t)B * DEC_MAX_WIN * L.split * 3 * cf.D * 4);
+  L.ppflag = o;    o = align256(o + (size_t)B * DEC_MAX_WIN * L.split * 4);
   L.total = o;
   return L;
 }
@@ -187,9 +189,8 @@ int check_args(const Cfg& cf, const compressor_args* a, bool decode) {
   if (a->out_rows > 0 && (!a->sin || !a->cos)) return CMP_ERR_NULLPTR;
   if (cf.rotate && !a->hadamard) return CMP_ERR_NULLPTR;
   if (decode) {
-    if (a->cu_seqlens) return CMP_ERR_INVALID;
-    if (a->T != a->batch) return CMP_ERR_INVALID;
-    if (a->batch > kDecodeMaxBatch) return CMP_ERR_UNSUPPORTED;
+    if (!a->cu_seqlens && a->T != a->batch) return CMP_ERR_INVALID;
+    if (a->batch > kDecodeMaxBatch || a->T > kDecodeMaxRows) return CMP_ERR_UNSUPPORTED;
   } else if (!a->cu_seqlens && a->T % a->batch) {
     return CMP_ERR_INVALID;
   }
@@ -389,28 +390,44 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
   const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
   const int B = a->batch;
   const int steps = cf.H / 16 / (L.ks * 4);
-  const dim3 gg(B * L.split + cf.N / 32 * L.ks);
+  const int T = a->T;
+  // the most windows a request can complete: its tokens (one without
+  // cu_seqlens, else at most 4 and at most T) span ceil(tokens / ratio)
+  const int max_tok = a->cu_seqlens ? std::min(T, DEC_MAX_TOK) : 1;
+  const int nwin = std::max(1, std::min(DEC_MAX_WIN, (max_tok + cf.ratio - 1) / cf.ratio));
+  const dim3 gg(B * nwin * L.split + cf.N / 32 * L.ks);
   CMP_TRY(launch("decode_main", st, [&] {
     const uint16_t* X = static_cast<const uint16_t*>(a->x);
     const uint16_t* W = static_cast<const uint16_t*>(a->w_packed);
     decltype(&decode_main_kernel<1, 4, 2>) kern = nullptr;
     with_ratio(cf.ratio, [&]<int R>() {
-      kern = B <= 32 ? decode_main_kernel<1, R, coff_of<R>()> : decode_main_kernel<2, R, coff_of<R>()>;
+      kern = T <= 32 ? decode_main_kernel<1, R, coff_of<R>()> : decode_main_kernel<2, R, coff_of<R>()>;
     });
-    hipLaunchKernelGGL(kern, gg, dim3(GV_THREADS), 0, st, cf, X, W, partial, B, steps, a->seqused,
-                       a->start_pos, a->kv_state, a->score_state, kvt, a->state_block_table, pp,
-                       ppflag, err);
+    hipLaunchKernelGGL(kern, gg, dim3(GV_THREADS), 0, st, cf, X, W, partial, B, T, nwin, steps,
+                       a->cu_seqlens, a->seqused, a->start_pos, a->kv_state, a->score_state, kvt,
+                       a->state_block_table, pp, ppflag, err);
   }));
   return launch("decode_tail", st, [&] {
-    decltype(&decode_tail_kernel<4, 2>) tail = nullptr;
-    with_ratio(cf.ratio, [&]<int R>() { tail = decode_tail_kernel<R, coff_of<R>()>; });
-    hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, L.ks, B,
-                       a->seqused, a->start_pos, a->ape, a->kv_state, a->score_state, kvt,
-                       a->state_block_table, pp, ppflag,
-                       static_cast<const uint16_t*>(a->norm_weight),
-                       static_cast<const uint16_t*>(a->cos), static_cast<const uint16_t*>(a->sin),
-                       static_cast<const uint16_t*>(a->hadamard), static_cast<uint16_t*>(a->out),
-                       a->out_rows, err);
+    const uint16_t* gamma = static_cast<const uint16_t*>(a->norm_weight);
+    const uint16_t* cosv = static_cast<const uint16_t*>(a->cos);
+    const uint16_t* sinv = static_cast<const uint16_t*>(a->sin);
+    const uint16_t* had = static_cast<const uint16_t*>(a->hadamard);
+    uint16_t* out = static_cast<uint16_t*>(a->out);
+    if (a->cu_seqlens) {
+      decltype(&decode_tail_kernel<4, 2>) tail = nullptr;
+      with_ratio(cf.ratio, [&]<int R>() { tail = decode_tail_kernel<R, coff_of<R>()>; });
+      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, L.ks, B, T,
+                         a->cu_seqlens, a->seqused, a->start_pos, a->ape, a->kv_state,
+                         a->score_state, kvt, a->state_block_table, pp, ppflag, gamma, cosv,
+                         sinv, had, out, a->out_rows, err);
+    } else {
+      decltype(&decode_tail1_kernel<4, 2>) tail = nullptr;
+      with_ratio(cf.ratio, [&]<int R>() { tail = decode_tail1_kernel<R, coff_of<R>()>; });
+      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, L.ks, B,
+                         a->seqused, a->start_pos, a->ape, a->kv_state, a->score_state, kvt,
+                         a->state_block_table, pp, ppflag, gamma, cosv, sinv, had, out,
+                         a->out_rows, err);
+    }
   });
 }
 

@@ -64,19 +64,53 @@ __device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp,
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
 }
 
-// Ring pre-pooling: workgroups of the decode main kernel that pool, for a
-// request whose token completes a window, every slot of that window except
-// the token itself ([PyPTO] 压缩窗口与状态更新; [CANN] 计算公式 steps 3-5):
-// per channel the softmax statistics (max m, sum l, weighted sum x) of those
-// slots.  None of them depends on this call's projection, so they run while
-// the GEMV streams the panel.  A window of more than 16 slots is split over
-// workgroups of 16 slots (C128A: 8 of them); smaller windows take one.
+// ---------------------------------------------------------------------------
+// Requests of a decode call: request b owns packed rows [cu[b], cu[b] + n_b)
+// of x (cu = cu_seqlens, or one row per request when it is NULL), n_b =
+// seqused[b] (or the slot length) tokens at positions s_b .. s_b + n_b - 1,
+// with n_b <= DEC_MAX_TOK ([PyPTO] 参数说明: S of a decode call is small).
+// Invalid values set an error bit and make the request empty.
+// ---------------------------------------------------------------------------
+constexpr int DEC_MAX_TOK = 4;
+constexpr int DEC_MAX_WIN = 2;               // windows a request completes: <= ceil(4 / 2)
+
+struct DecReq {
+  int s, n, row0;
+  uint32_t bad;
+};
+__device__ __forceinline__ DecReq dec_request(int b, int T, const int32_t* __restrict__ cu,
+                                              const int32_t* __restrict__ seqused,
+                                              const int32_t* __restrict__ start_pos) {
+  DecReq q{0, 0, 0, 0u};
+  int c0 = b, c1 = b + 1;
+  if (cu) { c0 = cu[b]; c1 = cu[b + 1]; }
+  if (c0 < 0 || c1 < c0 || c1 > T) { q.bad |= CMP_DEVERR_SEQLEN; return q; }
+  int n = seqused ? seqused[b] : c1 - c0;
+  if (n < 0 || n > c1 - c0 || n > DEC_MAX_TOK) { q.bad |= CMP_DEVERR_SEQLEN; return q; }
+  const int s = start_pos ? start_pos[b] : 0;
+  if (s < 0 || s > 0x7fffffff - DEC_MAX_TOK) { q.bad |= CMP_DEVERR_START_POS; return q; }
+  q.s = s;
+  q.n = n;
+  q.row0 = c0;
+  return q;
+}
+
+// Ring pre-pooling: workgroups of the decode main kernel that pool, for each
+// window a request completes in this call, the window's slots at positions
+// before the call (from the state ring; [PyPTO] 压缩窗口与状态更新; [CANN]
+// 计算公式 steps 3-5): per channel the softmax statistics (max m, sum l,
+// weighted sum x) of those slots.  None of them depends on this call's
+// projection, so they run while the GEMV streams the panel.  A window of
+// more than 16 slots is split over workgroups of 16 slots (C128A: 8 of
+// them); smaller windows take one.  Workgroup (b, k, sp) handles split sp of
+// request b's k-th completed window.
 constexpr int DEC_MAX_KSPLIT = 20;           // K ranges of the GEMV (H / 512 at most)
 template <int R>
 constexpr int dec_split() { return R <= 16 ? 1 : R / 16; }
 
 template <int R, int COFF>
-__device__ __forceinline__ void prepool_block(const Cfg& cf, int b, int sp,
+__device__ __forceinline__ void prepool_block(const Cfg& cf, int b, int k, int sp, int T,
+                                              const int32_t* __restrict__ cu,
                                               const int32_t* __restrict__ seqused,
                                               const int32_t* __restrict__ start_pos,
                                               const float* __restrict__ kv_state,
@@ -85,78 +119,84 @@ __device__ __forceinline__ void prepool_block(const Cfg& cf, int b, int sp,
                                               const int32_t* __restrict__ st_tab,
                                               float* __restrict__ pp, int32_t* __restrict__ ppflag) {
   constexpr int NSPLIT = dec_split<R>();
-  constexpr int NS = COFF * R / NSPLIT;          // slots per workgroup (8 or 16)
-  const int n = seqused ? seqused[b] : 1;
-  const int s = start_pos ? start_pos[b] : 0;
-  if (n != 1 || s < 0 || s == 0x7fffffff || (s + 1) % R != 0) return;   // nothing to pool
-  const int w = (s + 1) / R - 1;
+  constexpr int NS = COFF * R / NSPLIT;          // slots per workgroup
+  const DecReq q = dec_request(b, T, cu, seqused, start_pos);
+  const int s = q.s, e = q.s + q.n;
+  const int w = s / R + k;
+  if (q.n == 0 || w >= e / R) return;            // no k-th window in this call
   const int D = cf.D, cD = COFF * D;
   // slot j of the window: C4A j < 4 -> first set of position (w-1)*4 + j,
-  // j >= 4 -> second set of position w*4 + j - 4; C128A -> position w*128 + j
+  // j >= 4 -> second set of position w*4 + j - 4; coff 1 -> position w*R + j
   long rk[NS], rs[NS];
   bool use[NS];
   uint32_t bad = 0;
 #pragma unroll
-  for (int q = 0; q < NS; ++q) {
-    const int j = sp * NS + q;
+  for (int t = 0; t < NS; ++t) {
+    const int j = sp * NS + t;
     const int cs = COFF == 2 ? (j >= R) : 0;
     const int p = COFF == 2 ? (w - 1 + cs) * R + (j - cs * R) : w * R + j;
-    use[q] = p >= 0 && p != s;
-    rk[q] = 0;
-    rs[q] = 0;
-    if (use[q] && (!state_row(cf, kv_tab, b, p, &rk[q]) || !state_row(cf, st_tab, b, p, &rs[q]))) {
+    use[t] = p >= 0 && p < s;                    // this call's tokens come later
+    rk[t] = 0;
+    rs[t] = 0;
+    if (use[t] && (!state_row(cf, kv_tab, b, p, &rk[t]) || !state_row(cf, st_tab, b, p, &rs[t]))) {
       bad |= CMP_DEVERR_TABLE;
-      use[q] = false;
+      use[t] = false;
     }
   }
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
     float kv[NS], z[NS];
 #pragma unroll
-    for (int q = 0; q < NS; ++q) {
-      const int j = sp * NS + q;
+    for (int t = 0; t < NS; ++t) {
+      const int j = sp * NS + t;
       const int cs = COFF == 2 ? (j >= R) : 0;
-      kv[q] = use[q] ? kv_state[rk[q] * cD + cs * D + c] : 0.f;
-      z[q] = use[q] ? score_state[rs[q] * cD + cs * D + c] : -INFINITY;
+      kv[t] = use[t] ? kv_state[rk[t] * cD + cs * D + c] : 0.f;
+      z[t] = use[t] ? score_state[rs[t] * cD + cs * D + c] : -INFINITY;
     }
     float m = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < NS; ++q) m = fmaxf(m, z[q]);
+    for (int t = 0; t < NS; ++t) m = fmaxf(m, z[t]);
     float l = 0.f, x = 0.f;
     if (m != -INFINITY) {
 #pragma unroll
-      for (int q = 0; q < NS; ++q) {
-        const float e = __expf(z[q] - m);      // exp(-inf) = 0 for empty slots
-        l += e;
-        x = fmaf(e, kv[q], x);
+      for (int t = 0; t < NS; ++t) {
+        const float ex = __expf(z[t] - m);       // exp(-inf) = 0 for empty slots
+        l += ex;
+        x = fmaf(ex, kv[t], x);
       }
     }
-    float* o = pp + ((size_t)(b * NSPLIT + sp) * 3) * D + c;
+    float* o = pp + ((size_t)((b * DEC_MAX_WIN + k) * NSPLIT + sp) * 3) * D + c;
     o[0] = m;
     o[D] = l;
     o[2 * D] = x;
   }
-  if (threadIdx.x == 0) ppflag[b * NSPLIT + sp] = (int32_t)bad;
+  if (threadIdx.x == 0) ppflag[(b * DEC_MAX_WIN + k) * NSPLIT + sp] = (int32_t)bad;
 }
 
-// Decode main kernel.  Workgroups [0, B * split) pre-pool ring windows
-// (prepool_block); the rest run the GEMV: workgroup g owns column block
-// g % (N / 32) and K range g / (N / 32), its 4 waves divide the range, reduce
-// through LDS in a fixed order and write one fp32 partial per K range.
+// Decode main kernel.  Workgroups [0, B * nwin * split) pre-pool ring windows
+// (prepool_block; nwin <= DEC_MAX_WIN is the most windows a request can
+// complete in this call); the rest run the GEMV over the T packed rows:
+// workgroup g owns column block g % (N / 32) and K range g / (N / 32), its 4
+// waves divide the range, reduce through LDS in a fixed order and write one
+// fp32 partial per K range.
 template <int NRB, int R, int COFF>
 __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
     Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
-    float* __restrict__ partial, int B, int steps_per_wave,
-    const int32_t* __restrict__ seqused, const int32_t* __restrict__ start_pos,
+    float* __restrict__ partial, int B, int T, int nwin, int steps_per_wave,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ seqused,
+    const int32_t* __restrict__ start_pos,
     const float* __restrict__ kv_state, const float* __restrict__ score_state,
     const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
     float* __restrict__ pp, int32_t* __restrict__ ppflag, uint32_t* __restrict__ err) {
   // per wave: the x rows of a run, then (after the runs) its accumulators
-  __shared__ __attribute__((aligned(1024))) uint8_t xstage[4][NRB * 32 * 16 * 32];
+  constexpr int RUN = 16 / NRB;                  // k-steps per run: 16 KiB of x per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t xstage[4][NRB * 32 * RUN * 32];
   constexpr int NSPLIT = dec_split<R>();
-  const int npre = B * NSPLIT;
+  const int npre = B * nwin * NSPLIT;
   if ((int)blockIdx.x < npre) {
-    prepool_block<R, COFF>(cf, blockIdx.x / NSPLIT, blockIdx.x % NSPLIT, seqused, start_pos,
-                           kv_state, score_state, kv_tab, st_tab, pp, ppflag);
+    const int idx = blockIdx.x;
+    prepool_block<R, COFF>(cf, idx / (nwin * NSPLIT), (idx / NSPLIT) % nwin,
+                           idx % NSPLIT, T, cu, seqused, start_pos, kv_state, score_state, kv_tab,
+                           st_tab, pp, ppflag);
     return;
   }
   const int g = blockIdx.x - npre;
@@ -165,6 +205,7 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
   const int cb = g % ncb, kr = g / ncb;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (g == 0 && tid == 0) *err = 0;   // this call's error word (only the tail sets bits)
+  if (T == 0) return;
   const int kstep0 = (kr * 4 + wave) * steps_per_wave;
   // fragment (column block cb, k-step kstep0 + u) is 1 KiB contiguous
   const uint16_t* wp = W + (((size_t)cb * (K >> 4) + kstep0) * 64 + lane) * 8;
@@ -178,8 +219,11 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
     for (int r = 0; r < 16; ++r) acc[rb][r] = 0.f;
 
   int s = 0;
-  for (; s + 16 <= steps_per_wave; s += 16) gemv_run<16, NRB>(wp, xk, K, B, s, xl, acc);
-  if (s < steps_per_wave) gemv_run<8, NRB>(wp, xk, K, B, s, xl, acc);
+  // (every wave's share is a multiple of 8 k-steps)
+  for (; s + RUN <= steps_per_wave; s += RUN) gemv_run<RUN, NRB>(wp, xk, K, T, s, xl, acc);
+  if constexpr (RUN > 8) {
+    if (s < steps_per_wave) gemv_run<8, NRB>(wp, xk, K, T, s, xl, acc);
+  }
   float* red = reinterpret_cast<float*>(xl);            // [NRB * 16][64] of this wave
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
@@ -195,31 +239,309 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
     const int rb = reg >> 4, r = reg & 15;
     const int row = rb * 32 + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
     const int col = cb * 32 + (ln & 31);
-    if (row < B) partial[((size_t)kr * B + row) * N + col] = v;
+    if (row < T) partial[((size_t)kr * T + row) * N + col] = v;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Decode tail: one workgroup per request b, thread c owns channel c.
-//  1. the token's kv and score of channel c in every channel set: the K-range
-//     partials summed in a fixed order, Ape added to the score of position
-//     s = start_pos[b];
-//  2. if the token completes a window: merge the token's slot into the
-//     pre-pooled statistics of the window's other slots and take the pooled
-//     value ([PyPTO] 压缩窗口与状态更新; [CANN] 计算公式 steps 3-5), then
-//     RMSNorm, RoPE on the last 64 channels and the optional Hadamard
-//     product, stored to output row o_b; otherwise row o_b is +0 ([PyPTO]
-//     返回值说明);
-//  3. store the token's kv / score into ring slot s mod (coff*r) unless a
-//     coff = 1 window just closed (no later window pools it).  The main kernel
-//     has finished every read of the ring before this kernel starts.
-// Output rows: o_b = number of active requests before b (one ballot, B <= 64).
-// Workgroup B zero-fills the rows after the last request's.
+//  1. the kv and score of channel c of each of the request's n_b tokens in
+//     every channel set: the K-range partials summed in a fixed order, Ape
+//     added to the score of position p (row p mod r);
+//  2. for each window the tokens complete ([PyPTO] 压缩窗口与状态更新; [CANN]
+//     计算公式 steps 3-5): the pre-pooled statistics of its slots before the
+//     call merged with its slots among this call's tokens, then RMSNorm, RoPE
+//     on the last 64 channels and the optional Hadamard product, stored to
+//     output row o_b + k; the request's other rows (up to o_b + ceil(n_b/r))
+//     are +0 ([PyPTO] 返回值说明);
+//  3. the tokens' state rows that stay live ([max(s, r*floor(e/r) -
+//     (coff-1)*r), e)) into their ring slots.  The main kernel has finished
+//     every read of the ring before this kernel starts.
+// Output rows: o_b = sum over earlier requests of ceil(n/r) (one wave-wide
+// scan, B <= 64).  Workgroup B zero-fills the rows after the last request's.
 // ---------------------------------------------------------------------------
 constexpr int TL_THREADS = 512;
 
+// kv and score (before Ape) of channel c of packed row `row`, in every
+// channel set: the K-range partials, all loads in flight, summed in K order
+template <int COFF>
+__device__ __forceinline__ void dec_token_values(const float* __restrict__ partial, int row, int T,
+                                                 int N, int KS, int c, float (&kv)[COFF],
+                                                 float (&z)[COFF]) {
+  const size_t kstride = (size_t)T * N;
+  const float* pb = partial + (size_t)row * N;
+  float pk[COFF][DEC_MAX_KSPLIT], pz[COFF][DEC_MAX_KSPLIT];
+#pragma unroll
+  for (int cs = 0; cs < COFF; ++cs) {
+    const int ck = packed_col(0, cs, c, COFF), cz = packed_col(1, cs, c, COFF);
+#pragma unroll
+    for (int ks = 0; ks < DEC_MAX_KSPLIT; ++ks) {
+      pk[cs][ks] = ks < KS ? pb[ks * kstride + ck] : 0.f;
+      pz[cs][ks] = ks < KS ? pb[ks * kstride + cz] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int cs = 0; cs < COFF; ++cs) {
+    kv[cs] = 0.f;
+    z[cs] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DEC_MAX_KSPLIT; ++ks) {
+      kv[cs] += pk[cs][ks];
+      z[cs] += pz[cs][ks];
+    }
+  }
+}
+
 template <int R, int COFF>
 __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
+    Cfg cf, const float* __restrict__ partial, int KS, int B, int T,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ seqused,
+    const int32_t* __restrict__ start_pos, const float* __restrict__ ape,
+    float* __restrict__ kv_state, float* __restrict__ score_state,
+    const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
+    const float* __restrict__ pp, const int32_t* __restrict__ ppflag,
+    const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ cosv,
+    const uint16_t* __restrict__ sinv, const uint16_t* __restrict__ had, uint16_t* __restrict__ out,
+    int out_rows, uint32_t* __restrict__ err) {
+  constexpr int NSPLIT = dec_split<R>();
+  __shared__ float red[TL_THREADS / 64];
+  __shared__ float yv[512];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int D = cf.D, cD = COFF * D;
+  const int b = blockIdx.x;
+  const int c = tid;
+  const bool own = c < D && b < B;
+  const bool packed = cu != nullptr;
+
+  // loads that need no request record, issued first: with one row per
+  // request, token 0's partials (row b); the first window's pre-pooled
+  // statistics; the norm weight
+  float kvt[DEC_MAX_TOK][COFF], zt[DEC_MAX_TOK][COFF];
+#pragma unroll
+  for (int t = 0; t < DEC_MAX_TOK; ++t)
+#pragma unroll
+    for (int cs = 0; cs < COFF; ++cs) { kvt[t][cs] = 0.f; zt[t][cs] = 0.f; }
+  if (own && !packed) dec_token_values<COFF>(partial, b, T, cf.N, KS, c, kvt[0], zt[0]);
+  float pm0[NSPLIT], pl0[NSPLIT], px0[NSPLIT];
+#pragma unroll
+  for (int sp = 0; sp < NSPLIT; ++sp) {
+    pm0[sp] = -INFINITY;
+    pl0[sp] = 0.f;
+    px0[sp] = 0.f;
+  }
+  if (own) {
+#pragma unroll
+    for (int sp = 0; sp < NSPLIT; ++sp) {
+      const float* st = pp + ((size_t)(b * DEC_MAX_WIN * NSPLIT + sp) * 3) * D + c;
+      pm0[sp] = st[0];
+      pl0[sp] = st[D];
+      px0[sp] = st[2 * D];
+    }
+  }
+  const float g = own ? bf2f(gamma[c]) : 0.f;
+
+  // request records (lane j holds request j; B <= 64) and their output rows,
+  // scanned across the wave
+  DecReq qj{0, 0, 0, 0u};
+  if (lane < B) qj = dec_request(lane, T, cu, seqused, start_pos);
+  const int u = (qj.n + R - 1) / R;
+  int incl = u;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  const int total = __shfl(incl, 63, 64);
+
+  if ((int)blockIdx.x == B) {                    // rows after the last request's
+    if (total > out_rows && tid == 0) set_error(err, CMP_DEVERR_OUT_ROWS);
+    for (long i = (long)total * D + tid; i < (long)out_rows * D; i += TL_THREADS) out[i] = 0;
+    return;
+  }
+  // request b's record from lane b
+  const int o = __shfl(incl - u, b, 64);         // exclusive prefix of request b
+  DecReq q;
+  q.s = __shfl(qj.s, b, 64);
+  q.n = __shfl(qj.n, b, 64);
+  q.row0 = __shfl(qj.row0, b, 64);
+  q.bad = (uint32_t)__shfl((int)qj.bad, b, 64);
+  if (q.bad && tid == 0) set_error(err, q.bad);
+  const int n = q.n, s = q.s, e = s + n;
+  if (n == 0) return;
+  const int ub = (n + R - 1) / R;
+  if (o + ub > out_rows) {
+    if (tid == 0) set_error(err, CMP_DEVERR_OUT_ROWS);
+    return;
+  }
+  const int w0 = s / R, nwin = e / R - w0;       // windows completed here (<= 2)
+  // the ring rows of the tokens whose state stays live, looked up now so the
+  // stores at the end do not wait for the tables
+  const int lo = max(s, R * (e / R) - (COFF - 1) * R);
+  long srk[DEC_MAX_TOK], srs[DEC_MAX_TOK];
+  bool sok[DEC_MAX_TOK];
+  uint32_t tbad = 0;
+#pragma unroll
+  for (int t = 0; t < DEC_MAX_TOK; ++t) {
+    const int p = s + t;
+    srk[t] = 0;
+    srs[t] = 0;
+    sok[t] = t < n && p >= lo;
+    if (sok[t] && !(state_row(cf, kv_tab, b, p, &srk[t]) && state_row(cf, st_tab, b, p, &srs[t]))) {
+      tbad |= CMP_DEVERR_TABLE;
+      sok[t] = false;
+    }
+  }
+
+  const int rope0 = D - cf.rope;
+  const bool rope_lane = own && c >= rope0;
+  const int col = rope_lane ? ((c - rope0) >> 1) + ((c & 1) ? cf.rope / 2 : 0) : 0;
+  // the first window's rotary values (a second window, possible only at
+  // ratio 2, loads its own in the loop)
+  float rc0 = 0.f, rs0 = 0.f;
+  if (nwin > 0 && rope_lane) {
+    rc0 = bf2f(cosv[(size_t)o * cf.rope + col]);
+    rs0 = bf2f(sinv[(size_t)o * cf.rope + col]);
+  }
+
+  // 1. the tokens' projected values of channel c (packed rows: one token
+  //    after the other), then Ape on the scores
+  if (own) {
+    if (packed) {
+#pragma unroll
+      for (int t = 0; t < DEC_MAX_TOK; ++t) {
+        if (t >= n) break;
+        dec_token_values<COFF>(partial, q.row0 + t, T, cf.N, KS, c, kvt[t], zt[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < DEC_MAX_TOK; ++t) {
+      if (t >= n) break;
+#pragma unroll
+      for (int cs = 0; cs < COFF; ++cs) zt[t][cs] += ape[(long)((s + t) % R) * cD + cs * D + c];
+    }
+  }
+  // 2. the completed windows
+  for (int k = 0; k < nwin; ++k) {
+    const int w = w0 + k;
+    if (tid < NSPLIT) {
+      const int32_t f = ppflag[(b * DEC_MAX_WIN + k) * NSPLIT + tid];
+      if (f) set_error(err, (uint32_t)f);
+    }
+    float pooled = 0.f;
+    if (own) {
+      float pm[NSPLIT], pl[NSPLIT], px[NSPLIT];
+#pragma unroll
+      for (int sp = 0; sp < NSPLIT; ++sp) {
+        if (k == 0) {
+          pm[sp] = pm0[sp];
+          pl[sp] = pl0[sp];
+          px[sp] = px0[sp];
+        } else {
+          const float* st = pp + ((size_t)((b * DEC_MAX_WIN + k) * NSPLIT + sp) * 3) * D + c;
+          pm[sp] = st[0];
+          pl[sp] = st[D];
+          px[sp] = st[2 * D];
+        }
+      }
+      // this call's tokens in the window and their channel set: C4A first
+      // set for positions (w-1)*4 .. w*4-1, second set for w*4 .. w*4+3
+      float zs[DEC_MAX_TOK], ks_[DEC_MAX_TOK];
+      bool in[DEC_MAX_TOK];
+#pragma unroll
+      for (int t = 0; t < DEC_MAX_TOK; ++t) {
+        const int p = s + t;
+        const int lo = (w - (COFF - 1)) * R, hi = (w + 1) * R;
+        in[t] = t < n && p >= lo && p < hi;
+        const int cs = COFF == 2 ? (p >= w * R) : 0;
+        zs[t] = cs ? zt[t][COFF - 1] : zt[t][0];
+        ks_[t] = cs ? kvt[t][COFF - 1] : kvt[t][0];
+        if (in[t] && zs[t] == -INFINITY) in[t] = false;
+      }
+      float m = -INFINITY;
+#pragma unroll
+      for (int sp = 0; sp < NSPLIT; ++sp) if (pl[sp] > 0.f) m = fmaxf(m, pm[sp]);
+#pragma unroll
+      for (int t = 0; t < DEC_MAX_TOK; ++t) if (in[t]) m = fmaxf(m, zs[t]);
+      float l = 0.f, x = 0.f;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int t = 0; t < DEC_MAX_TOK; ++t) {
+          if (!in[t]) continue;
+          const float ex = __expf(zs[t] - m);
+          l += ex;
+          x = fmaf(ex, ks_[t], x);
+        }
+#pragma unroll
+        for (int sp = 0; sp < NSPLIT; ++sp) {
+          if (pl[sp] > 0.f) {
+            const float sc = __expf(pm[sp] - m);
+            l = fmaf(pl[sp], sc, l);
+            x = fmaf(px[sp], sc, x);
+          }
+        }
+      }
+      pooled = l > 0.f ? x / l : 0.f;
+    }
+    // RMSNorm over the D channels (block-wide sum)
+    float v = own ? pooled * pooled : 0.f;
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float ss = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < TL_THREADS / 64; ++qq) ss += red[qq];
+    __syncthreads();                             // red is reused by the next window
+    const float inv = rsqrtf(ss / float(D) + kRmsEps);
+    float y = own ? pooled * inv * g : 0.f;
+    // RoPE: pair (2i, 2i+1) of the trailing rope slice, partner via lane ^ 1;
+    // the even element takes cos/sin column i, the odd one column 32 + i
+    const float partner = __shfl_xor(y, 1, 64);
+    const int orow = o + k;
+    if (rope_lane) {
+      const float rc = k == 0 ? rc0 : bf2f(cosv[(size_t)orow * cf.rope + col]);
+      const float rsn = k == 0 ? rs0 : bf2f(sinv[(size_t)orow * cf.rope + col]);
+      y = (c & 1) == 0 ? y * rc - partner * rsn : y * rc + partner * rsn;
+    }
+    uint16_t* op = out + (size_t)orow * D;
+    if (!cf.rotate) {
+      if (own) op[c] = f2bf(y);
+    } else {
+      if (own) yv[c] = y;
+      __syncthreads();
+      if (own) {
+        float acc = 0.f;
+#pragma unroll 8
+        for (int i2 = 0; i2 < D; ++i2) acc += yv[i2] * bf2f(had[(size_t)i2 * D + c]);
+        op[c] = f2bf(acc);
+      }
+      __syncthreads();                           // yv is reused by the next window
+    }
+  }
+  // the request's rows without a window
+  for (int k = nwin; k < ub; ++k)
+    if (own) out[(size_t)(o + k) * D + c] = 0;
+
+  // 3. the tokens' state rows that stay live
+  if (own) {
+#pragma unroll
+    for (int t = 0; t < DEC_MAX_TOK; ++t) {
+      if (!sok[t]) continue;
+#pragma unroll
+      for (int cs = 0; cs < COFF; ++cs) {
+        kv_state[srk[t] * cD + cs * D + c] = kvt[t][cs];
+        score_state[srs[t] * cD + cs * D + c] = zt[t][cs];
+      }
+    }
+  }
+  if (tbad && tid == 0) set_error(err, tbad);
+}
+
+// Decode tail for one row per request (no cu_seqlens): the general tail
+// below specialised to a single token, so every load it needs is issued at
+// once (the token's partials, the pre-pooled statistics, the norm weight,
+// rotary values and state tables); same steps and results.
+template <int R, int COFF>
+__global__ __launch_bounds__(TL_THREADS) void decode_tail1_kernel(
     Cfg cf, const float* __restrict__ partial, int KS, int B, const int32_t* __restrict__ seqused,
     const int32_t* __restrict__ start_pos, const float* __restrict__ ape,
     float* __restrict__ kv_state, float* __restrict__ score_state,
@@ -234,8 +556,11 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int D = cf.D, cD = COFF * D;
 
-  // active requests (one token each) as a 64-bit mask, identical in every wave
-  const bool act = lane < B && (seqused ? seqused[lane] == 1 : true);
+  // active requests (one valid token each) as a 64-bit mask, identical in
+  // every wave; a request with an invalid start position is empty
+  const int sl = lane < B && start_pos ? start_pos[lane] : 0;
+  const bool act = lane < B && (seqused ? seqused[lane] == 1 : true) && sl >= 0 &&
+                   sl <= 0x7fffffff - DEC_MAX_TOK;
   const unsigned long long amask = __ballot(act);
   const int total = __popcll(amask);
 
@@ -250,7 +575,7 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
   int s = start_pos ? start_pos[b] : 0;
   uint32_t bad = 0;
   if (n < 0 || n > 1) { bad |= CMP_DEVERR_SEQLEN; n = 0; }
-  if (s < 0 || s == 0x7fffffff) { bad |= CMP_DEVERR_START_POS; n = 0; s = 0; }
+  if (s < 0 || s > 0x7fffffff - DEC_MAX_TOK) { bad |= CMP_DEVERR_START_POS; n = 0; s = 0; }
   if (bad && tid == 0) set_error(err, bad);
   if (n == 0) return;
   if (o >= out_rows) {
@@ -295,7 +620,7 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
     if (completing) {
 #pragma unroll
       for (int q = 0; q < NSPLIT; ++q) {
-        const float* st = pp + ((size_t)(b * NSPLIT + q) * 3) * D + c;
+        const float* st = pp + ((size_t)(b * DEC_MAX_WIN * NSPLIT + q) * 3) * D + c;
         pm[q] = st[0];
         pl[q] = st[D];
         px[q] = st[2 * D];
@@ -303,7 +628,7 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
     }
   }
   if (completing && tid < NSPLIT) {
-    const int32_t f = ppflag[b * NSPLIT + tid];
+    const int32_t f = ppflag[b * DEC_MAX_WIN * NSPLIT + tid];
     if (f) set_error(err, (uint32_t)f);
   }
   // loads the later steps need, issued with the ones above: norm weight,

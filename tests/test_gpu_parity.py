@@ -199,8 +199,15 @@ def test_host_side_errors(harness):
         case.prefill(workspace=small)
     assert ei.value.status == 4
     with pytest.raises(cmp.CompressorError) as ei:
-        case.decode(cu_seqlens=case.cu_seqlens)
-    assert ei.value.status in (2, 3)
+        case.decode()                 # no cu_seqlens needs one row per request
+    assert ei.value.status == 2
+    # more than 64 packed rows is beyond the decode entry point
+    spec = dataclasses.replace(workloads.C4LI_SMALL, name="decode_rows", batch=2, lengths=(40, 40),
+                               tables="perm", spare_blocks=2, out_rows=20)
+    big = harness.DeviceCase(workloads.build(spec, workloads.SEED_BASE + 77))
+    with pytest.raises(cmp.CompressorError) as ei:
+        big.decode(cu_seqlens=big.cu_seqlens)
+    assert ei.value.status == 3
 
 
 # --------------------------------------------------------------------------

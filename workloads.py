@@ -229,6 +229,9 @@ DECODE_C128A = dataclasses.replace(DECODE_C4A, name="decode_c128a", ratio=128)
 # decode where every request completes a window (the step that emits output)
 DECODE_C4A_ALL = dataclasses.replace(DECODE_C4A, name="decode_c4a_all")
 DECODE_C128A_ALL = dataclasses.replace(DECODE_C128A, name="decode_c128a_all")
+# multi-token decode (two tokens per request per call, packed with cu_seqlens)
+DECODE_C4A_MTP2 = dataclasses.replace(DECODE_C4A, name="decode_c4a_mtp2", lengths=(2,),
+                                      out_rows=64)
 # variable-length packed prefill with continuation
 VARLEN_C4A = Spec("varlen_c4a", ratio=4, head_dim=512, hidden=4096, rotate=True,
                   block_size=256, batch=8, lengths=("uniform", 1, 16384),
@@ -244,7 +247,8 @@ P1_COMP_INDEXER = Spec("p1_comp_indexer", ratio=4, head_dim=128, hidden=4096, ro
                        block_size=128, batch=64, lengths=(2,), start_pos=(1,))
 
 ALL = {s.name: s for s in (C4LI_SMALL, C128A_8192, C128A_8269, C4A_128K, DECODE_C4A,
-                            DECODE_C128A, DECODE_C4A_ALL, DECODE_C128A_ALL, VARLEN_C4A,
+                            DECODE_C128A, DECODE_C4A_ALL, DECODE_C128A_ALL, DECODE_C4A_MTP2,
+                            VARLEN_C4A,
                             VARLEN_C4A_PADDED, P1_COMP_128, P1_COMP_4, P1_COMP_INDEXER)}
 CONFIG_INDEX = {"c4li_small": 0, "c128a_8192": 1, "c128a_8269": 1, "c4a_128k": 2,
                 "decode_c4a": 3, "decode_c128a": 3, "decode_c4a_all": 3,

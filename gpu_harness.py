@@ -96,3 +96,40 @@ class DeviceCase:
 
     def states(self):
         return self.kv_state.cpu().numpy(), self.score_state.cpu().numpy()
+
+
+class NsaCase:
+    """One NSA compression call on the device (uploads a build_nsa dict)."""
+
+    def __init__(self, w: dict, device="cuda:0"):
+        self.w = w
+        self.dev = torch.device(device)
+        dt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float16
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.dev).view(dt)
+        self.input = up(w["input"])
+        self.weight = up(w["weight"])
+        self.out = up(w["output_cache"])
+        self.slots = torch.from_numpy(w["slot_mapping"]).to(self.dev)
+        self.lens = torch.from_numpy(w["act_seq_len"]).to(self.dev)
+        self.table = (torch.from_numpy(w["block_table"]).to(self.dev)
+                      if w["block_table"] is not None else None)
+        self.err = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        self.shape = cmp.make_nsa_shape(
+            w["head_num"], w["head_dim"], w["cbs"], w["stride"], w["page"],
+            cmp.NSA_F16 if w["dtype"] == "f16" else cmp.NSA_BF16,
+            cmp.NSA_LAYOUT_PAGED if w["layout"] == "paged" else cmp.NSA_LAYOUT_TND)
+
+    def run(self, **over):
+        kw = dict(input=self.input, weight=self.weight, slot_mapping=self.slots,
+                  act_seq_len=self.lens, output_cache=self.out, block_table=self.table,
+                  device_error=self.err)
+        kw.update(over)
+        cmp.nsa_compress_with_cache(self.shape, **kw)
+
+    def out_bits(self) -> np.ndarray:
+        torch.cuda.synchronize()
+        return self.out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def device_error(self) -> int:
+        torch.cuda.synchronize()
+        return int(self.err.item())

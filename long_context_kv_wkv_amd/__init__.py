@@ -25,7 +25,11 @@ DEVERR_TABLE, DEVERR_START_POS, DEVERR_SEQLEN, DEVERR_OUT_ROWS = 1, 2, 4, 8
 EXPORTS = ("compressor_prefill_workspace_size", "compressor_decode_workspace_size",
            "compressor_pack_weights", "compressor_state_init", "compressor_state_reset",
            "compressor_prefill", "compressor_decode", "compressor_last_device_error",
-           "compressor_status_str", "compressor_timing_enable", "compressor_timing_query")
+           "compressor_status_str", "compressor_timing_enable", "compressor_timing_query",
+           "nsa_compress_with_cache")
+NSA_BF16, NSA_F16 = 0, 1
+NSA_LAYOUT_PAGED, NSA_LAYOUT_TND = 0, 1
+NSA_DEVERR_SLOT, NSA_DEVERR_TABLE, NSA_DEVERR_SEQLEN = 1, 2, 4
 
 
 class CompressorError(RuntimeError):
@@ -57,6 +61,22 @@ class Args(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class NsaShape(ctypes.Structure):
+    _fields_ = [("head_num", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("compress_block_size", ctypes.c_int32), ("compress_stride", ctypes.c_int32),
+                ("page_block_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
+
+
+class NsaArgs(ctypes.Structure):
+    _fields_ = [("input", ctypes.c_void_p), ("weight", ctypes.c_void_p),
+                ("slot_mapping", ctypes.c_void_p), ("act_seq_len", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("table_stride", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("T", ctypes.c_int64), ("output_cache", ctypes.c_void_p),
+                ("result_len", ctypes.c_int64), ("device_error", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -81,6 +101,7 @@ def library():
             "compressor_timing_enable": (i32,),
             "compressor_timing_query": (ctypes.c_char_p, ctypes.POINTER(i32),
                                         ctypes.POINTER(ctypes.c_double)),
+            "nsa_compress_with_cache": (ctypes.POINTER(NsaShape), ctypes.POINTER(NsaArgs), vp),
         }
         for name, argt in sig.items():
             fn = getattr(lib, name)
@@ -217,3 +238,37 @@ def compressor_timing_query(kernel: str):
     _check("compressor_timing_query", library().compressor_timing_query(
         kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+# --------------------------------------------------------------------------
+# NSA KV compression (include/nsa_compress.h)
+# --------------------------------------------------------------------------
+def make_nsa_shape(head_num: int, head_dim: int, compress_block_size: int, compress_stride: int,
+                   page_block_size: int, dtype: int, layout: int) -> NsaShape:
+    return NsaShape(head_num, head_dim, compress_block_size, compress_stride, page_block_size,
+                    dtype, layout)
+
+
+def nsa_compress_with_cache(shape: NsaShape, *, input: torch.Tensor, weight: torch.Tensor,
+                            slot_mapping: torch.Tensor, act_seq_len: torch.Tensor,
+                            output_cache: torch.Tensor, block_table: torch.Tensor = None,
+                            device_error: torch.Tensor = None, stream=None) -> None:
+    """input / weight / output_cache: bf16 or fp16 tensors (their codes);
+    slot_mapping int32 [B]; act_seq_len int64 [B]; block_table int32
+    [B, stride] for the paged layout; device_error an int32 [1] word the
+    kernel ORs NSA_DEVERR_* bits into."""
+    dt = torch.float16 if shape.dtype == NSA_F16 else torch.bfloat16
+    paged = shape.layout == NSA_LAYOUT_PAGED
+    args = NsaArgs(_dev(input, dt, "input"), _dev(weight, dt, "weight"),
+                   _dev(slot_mapping, torch.int32, "slot_mapping"),
+                   _dev(act_seq_len, torch.int64, "act_seq_len"),
+                   _dev(block_table, torch.int32, "block_table") if paged else None,
+                   int(slot_mapping.numel()),
+                   int(block_table.shape[1]) if paged else 0,
+                   int(input.shape[0]) if paged else 0,
+                   0 if paged else int(input.shape[0]),
+                   _dev(output_cache, dt, "output_cache"), int(output_cache.shape[0]),
+                   _dev(device_error, torch.int32, "device_error"))
+    _check("nsa_compress_with_cache",
+           library().nsa_compress_with_cache(ctypes.byref(shape), ctypes.byref(args),
+                                             _stream(stream)))

@@ -10,11 +10,13 @@
 #include <vector>
 
 #include "compressor.h"
+#include "nsa_compress.h"
 #include "common.hpp"
 #include "decode.hpp"
 #include "gemm.hpp"
 #include "pool.hpp"
 #include "prefill.hpp"
+#include "nsa.hpp"
 
 using namespace cmp;
 
@@ -465,6 +467,47 @@ int compressor_timing_query(const char* kernel, int32_t* launches, double* total
   *launches = n;
   *total_ms = tot;
   return CMP_OK;
+}
+
+
+int nsa_compress_with_cache(const nsa_shape* sh, const nsa_args* a, void* stream) {
+  if (!sh || !a) return CMP_ERR_NULLPTR;
+  // [NSA] 约束说明
+  if (sh->head_num < 1 || sh->head_num > 64 || (sh->head_num > 50 && sh->head_num % 2))
+    return CMP_ERR_UNSUPPORTED;
+  if (sh->head_dim < 16 || sh->head_dim > 256 || sh->head_dim % 16) return CMP_ERR_UNSUPPORTED;
+  const int st = sh->compress_stride, cb = sh->compress_block_size;
+  if (st != 16 && st != 32 && st != 48 && st != 64) return CMP_ERR_UNSUPPORTED;
+  if (cb % 16 || cb < st || cb > 64) return CMP_ERR_UNSUPPORTED;
+  if (sh->page_block_size != 64 && sh->page_block_size != 128) return CMP_ERR_UNSUPPORTED;
+  if (sh->dtype != NSA_BF16 && sh->dtype != NSA_F16) return CMP_ERR_UNSUPPORTED;
+  if (sh->layout != NSA_LAYOUT_PAGED && sh->layout != NSA_LAYOUT_TND) return CMP_ERR_UNSUPPORTED;
+  if (!a->input || !a->weight || !a->slot_mapping || !a->act_seq_len || !a->output_cache)
+    return CMP_ERR_NULLPTR;
+  if (a->batch < 1 || a->result_len < 1) return CMP_ERR_INVALID;
+  const bool paged = sh->layout == NSA_LAYOUT_PAGED;
+  if (paged) {
+    if (!a->block_table) return CMP_ERR_NULLPTR;
+    if (a->table_stride < 1 || a->num_blocks < 1) return CMP_ERR_INVALID;
+  } else if (a->T < 0) {
+    return CMP_ERR_INVALID;
+  }
+  NsaCfg cf{sh->head_num, sh->head_dim, cb, st, sh->page_block_size, sh->dtype == NSA_F16,
+            paged ? 1 : 0};
+  const long E = (long)sh->head_num * sh->head_dim;
+  const dim3 grid(a->batch, (unsigned)((E + NSA_CHUNK - 1) / NSA_CHUNK));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch("nsa", s, [&] {
+    auto kern = cb == 16 ? nsa_compress_kernel<16>
+                : cb == 32 ? nsa_compress_kernel<32>
+                : cb == 48 ? nsa_compress_kernel<48> : nsa_compress_kernel<64>;
+    hipLaunchKernelGGL(kern, grid, dim3(NSA_THREADS), 0, s, cf,
+                       static_cast<const uint16_t*>(a->input),
+                       static_cast<const uint16_t*>(a->weight), a->slot_mapping, a->act_seq_len,
+                       a->block_table, a->batch, a->table_stride, a->num_blocks, (long)a->T,
+                       static_cast<uint16_t*>(a->output_cache), (long)a->result_len,
+                       a->device_error);
+  });
 }
 
 }  // extern "C"

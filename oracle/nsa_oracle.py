@@ -74,12 +74,15 @@ def token_rows(b, first, count, act_seq_len, block_table, page_block_size):
 
 
 def nsa_compress(inp, weight, slot_mapping, act_seq_len, block_table, out_cache, *, cbs, stride,
-                 page_block_size, dtype):
+                 page_block_size, dtype, absolute=False):
     """Returns (exact fp64 out cache values of written slots, the new cache
     codes, the list of (b, slot) written).  inp / weight / out_cache are codes
-    (uint16) of `dtype`."""
+    (uint16) of `dtype`.  absolute=True sums |token| * |weight| instead (the
+    scale of a rounding-error bound)."""
     x = decode_dtype(inp, dtype)
     w = decode_dtype(weight, dtype)                     # [cbs, N]
+    if absolute:
+        x, w = np.abs(x), np.abs(w)
     new = np.array(out_cache, dtype=np.uint16, copy=True)
     exact = {}
     written = []

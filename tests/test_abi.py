@@ -17,7 +17,8 @@ def declared_functions():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         src = open(h).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        names.update(re.findall(r"^(?:int|const char\*)\s+(compressor_\w+)\s*\(", src, flags=re.M))
+        names.update(re.findall(r"^(?:int|const char\*)\s+((?:compressor|nsa)_\w+)\s*\(", src,
+                                flags=re.M))
     return names
 
 
@@ -85,3 +86,21 @@ def test_null_arguments_rejected_before_any_launch():
     ms = ctypes.c_double()
     assert lib.compressor_timing_query(b"gemm", ctypes.byref(n), ctypes.byref(ms)) == 0
     assert n.value == 0
+
+
+def test_nsa_shape_checks_before_any_launch():
+    lib = cmp.library()
+    args = cmp.NsaArgs()                         # every pointer NULL
+    good = cmp.make_nsa_shape(32, 128, 32, 16, 128, cmp.NSA_BF16, cmp.NSA_LAYOUT_PAGED)
+    assert lib.nsa_compress_with_cache(ctypes.byref(good), ctypes.byref(args), None) == 1
+    for bad in (cmp.make_nsa_shape(65, 128, 32, 16, 128, 0, 0),    # too many heads
+                cmp.make_nsa_shape(51, 128, 32, 16, 128, 0, 0),    # odd head count above 50
+                cmp.make_nsa_shape(32, 136, 32, 16, 128, 0, 0),    # head_dim not a multiple of 16
+                cmp.make_nsa_shape(32, 272, 32, 16, 128, 0, 0),    # head_dim above 256
+                cmp.make_nsa_shape(32, 128, 80, 16, 128, 0, 0),    # window above 64
+                cmp.make_nsa_shape(32, 128, 16, 32, 128, 0, 0),    # window below stride
+                cmp.make_nsa_shape(32, 128, 32, 24, 128, 0, 0),    # stride not 16/32/48/64
+                cmp.make_nsa_shape(32, 128, 32, 16, 256, 0, 0),    # page size
+                cmp.make_nsa_shape(32, 128, 32, 16, 128, 2, 0),    # dtype
+                cmp.make_nsa_shape(32, 128, 32, 16, 128, 0, 2)):   # layout
+        assert lib.nsa_compress_with_cache(ctypes.byref(bad), ctypes.byref(args), None) == 3

@@ -267,3 +267,71 @@ def build_named(name: str, with_x: bool = True) -> dict:
         sp = w["start_pos"].astype(np.int64)
         w["start_pos"] = (sp - sp % r + (r - 1)).astype(np.int32)
     return w
+
+
+# --------------------------------------------------------------------------
+# NSA KV compression (NsaCompressWithCache) inputs
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class NsaSpec:
+    name: str
+    head_num: int
+    head_dim: int
+    cbs: int                 # compress block size
+    stride: int
+    page: int                # page block size
+    dtype: str               # "bf16" or "f16"
+    layout: str              # "paged" or "tnd"
+    batch: int
+    max_len: int             # lengths are drawn in [1, max_len]
+    fire_fraction: float     # share of batches whose length triggers a compression
+    slot_factor: int = 3     # result_len = slot_factor * batch
+
+
+def _codes(x: np.ndarray, dtype: str) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x.astype(np.float16).view(np.uint16)
+
+
+def build_nsa(spec: NsaSpec, seed: int) -> dict:
+    """Draw every input of one NSA compression call.  Draw order: lengths,
+    firing choice, cache values, block table, weight, slots, output cache."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, N, D = spec.batch, spec.head_num, spec.head_dim
+    lengths = rng.integers(1, spec.max_len + 1, size=B, dtype=np.int64)
+    fire = rng.random(B) < spec.fire_fraction
+    # a firing length is cbs + k * stride (<= max_len); the others are moved
+    # off that lattice
+    kmax = max((spec.max_len - spec.cbs) // spec.stride, 0)
+    ks = rng.integers(0, kmax + 1, size=B, dtype=np.int64)
+    lengths = np.where(fire, spec.cbs + ks * spec.stride, lengths)
+    hits = (lengths >= spec.cbs) & ((lengths - spec.cbs) % spec.stride == 0)
+    lengths = np.where(~fire & hits, lengths - 1, lengths)
+    lengths = np.maximum(lengths, 1)
+    if spec.layout == "paged":
+        per = -(-int(lengths.max()) // spec.page)
+        nblocks = B * per + 3
+        cache = normal_bf16(rng, (nblocks, spec.page, N, D), 1.0) if spec.dtype == "bf16" else \
+            _codes(rng.standard_normal((nblocks, spec.page, N, D), dtype=np.float32), "f16")
+        table = rng.permutation(nblocks)[: B * per].reshape(B, per).astype(np.int32)
+    else:
+        T = int(lengths.sum())
+        cache = normal_bf16(rng, (T, N, D), 1.0) if spec.dtype == "bf16" else \
+            _codes(rng.standard_normal((T, N, D), dtype=np.float32), "f16")
+        table = None
+    weight = _codes(rng.standard_normal((spec.cbs, N), dtype=np.float32)
+                    * np.float32(1.0 / math.sqrt(spec.cbs)), spec.dtype)
+    result_len = spec.slot_factor * B
+    slots = rng.permutation(result_len)[:B].astype(np.int32)
+    out_cache = _codes(rng.standard_normal((result_len, N, D), dtype=np.float32), spec.dtype)
+    return dict(name=spec.name, head_num=N, head_dim=D, cbs=spec.cbs, stride=spec.stride,
+                page=spec.page, dtype=spec.dtype, layout=spec.layout, batch=B,
+                act_seq_len=lengths.astype(np.int64), input=cache, block_table=table,
+                weight=weight, slot_mapping=slots, output_cache=out_cache,
+                result_len=result_len)
+
+
+# NSA decode step: 128 sequences that all compress (32-token window, stride
+# 16, 32 heads of 128), paged with 128-token pages
+NSA_DECODE = NsaSpec("nsa_decode", head_num=32, head_dim=128, cbs=32, stride=16, page=128,
+                     dtype="bf16", layout="paged", batch=128, max_len=256, fire_fraction=1.0)

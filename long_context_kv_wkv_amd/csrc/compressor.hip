@@ -119,6 +119,23 @@ void with_ratio(int r, F&& f) {
   }
 }
 
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cus;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cus.size() <= dev) cus.resize(dev + 1, 0);
+  if (cus[dev] == 0) {
+    hipDeviceProp_t prop;
+    cus[dev] = hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount >= 8
+                   ? prop.multiProcessorCount
+                   : 256;
+  }
+  return cus[dev];
+}
+
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct PrefillLayout {
@@ -210,7 +227,7 @@ int ensure_lds_limits() {
       with_ratio(r, [&]<int R>() {
         const hipError_t e = hipFuncSetAttribute(gemm_kernel_of<R>(),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 GM_LDS_BYTES);
+                                                 POOL_LDS_BYTES);
         if (e1 == hipSuccess) e1 = e;
       });
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(post_kernel<8>),
@@ -343,13 +360,15 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
                          a->kv_state, a->score_state, kvt, a->state_block_table, plan, staging,
                          err);
     }));
+    // persistent: one workgroup per CU (a multiple of 8, one run of tiles
+    // per XCD), never more than there are tiles
     const int tiles_n = cf.N / GM_BN;
     const long nwg = (long)prefill_max_tiles(cf, T, B) * tiles_n;
-    const int grid = int((nwg + 7) / 8 * 8);
+    const int grid = int(std::min<long>(device_cu_count() / 8 * 8, (nwg + 7) / 8 * 8));
     CMP_TRY(launch("gemm", st, [&] {
       decltype(&gemm_pool_kernel<4, 2>) kern = nullptr;
       with_ratio(cf.ratio, [&]<int R>() { kern = gemm_pool_kernel<R, coff_of<R>()>; });
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(GM_THREADS), GM_LDS_BYTES, st, cf,
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(GM_THREADS), POOL_LDS_BYTES, st, cf,
                          static_cast<const uint16_t*>(a->x),
                          static_cast<const uint16_t*>(a->w_packed), T, B, plan, tiles, a->ape,
                          staging, a->kv_state, a->score_state, kvt, a->state_block_table, pooled,

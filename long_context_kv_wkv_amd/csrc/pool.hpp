@@ -295,45 +295,61 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
   }
 }
 
+constexpr int POOL_LDS_BYTES = GM_LDS_BYTES + 1024;   // copy ring + epilogue exchange
+
+// One tile of a request: M-tile mt (its request b, the tile's first position
+// P0 and its index tloc among the request's tiles) and N-tile nt.
+struct PoolTile {
+  int mt, nt, b, tloc, P0, n0;
+  const int32_t* rec;
+};
+
+template <int R>
+__device__ __forceinline__ PoolTile pool_tile(int tile, int tiles_n, const int32_t* __restrict__ plan,
+                                              int B) {
+  PoolTile t;
+  t.mt = tile / tiles_n;
+  t.nt = tile - t.mt * tiles_n;
+  t.b = find_tile_request(plan, B, t.mt);
+  t.rec = plan + (long)t.b * PL_WIDTH;
+  t.tloc = t.mt - t.rec[PL_TILE0];
+  t.P0 = R * (t.rec[PL_START] / R) + t.tloc * GM_BM;
+  t.n0 = t.nt * GM_BN;
+  return t;
+}
+
+// The tile's copy sources: X rows of positions P0 + (tile row), clamped into x.
+__device__ __forceinline__ GmSrc pool_sources(const PoolTile& t, const Cfg& cf,
+                                              const uint16_t* __restrict__ X,
+                                              const uint16_t* __restrict__ W, int T) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int s = t.rec[PL_START], row0 = t.rec[PL_ROW0];
+  int arow[GM_A_COPIES];
+#pragma unroll
+  for (int j = 0; j < GM_A_COPIES; ++j) {
+    const int p = t.P0 + gm_copy_row(wave, lane, j);
+    arow[j] = min(max(row0 + (p - s), 0), T - 1);
+  }
+  return gm_sources(X, W, cf.H, t.n0, arow);
+}
+
+// Pooling epilogue of one tile (see the top of this file).  xch: 1 KiB of LDS
+// outside the copy ring.
 template <int R, int COFF>
-__global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
-    Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int T, int B,
-    const int32_t* __restrict__ plan, const int32_t* __restrict__ tile_count,
+__device__ __forceinline__ void pool_epilogue(
+    const Cfg& cf, const f32x16 (&acc)[4][4], uint8_t* xch, const PoolTile& tl,
     const float* __restrict__ ape, const float* __restrict__ staging,
     float* __restrict__ kv_state, float* __restrict__ score_state,
     const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
-    float* __restrict__ pooled, int out_rows, float* __restrict__ split,
-    uint32_t* __restrict__ err) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    float* __restrict__ pooled, int out_rows, float* __restrict__ split, uint32_t* __restrict__ err) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int lrow = lane & 31, h = lane >> 5;
-  const int tiles_n = cf.N / GM_BN;
-
-  // XCD-aware order: workgroup i runs on XCD i % 8; each XCD takes a
-  // contiguous run of tiles, N fastest, so the N-tiles of an M-tile (sharing
-  // its x rows) run together and share that XCD's L2.
-  const int per_xcd = gridDim.x >> 3;
-  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  const int mt = tile / tiles_n, nt = tile - mt * tiles_n;
-  if (mt >= *tile_count) return;
-  const int b = find_tile_request(plan, B, mt);
-  const int32_t* rec = plan + (long)b * PL_WIDTH;
-  const int s = rec[PL_START], e = rec[PL_END], row0 = rec[PL_ROW0];
-  const int tloc = mt - rec[PL_TILE0];
-  const int P0 = R * (s / R) + tloc * GM_BM;
-  const int n0 = nt * GM_BN;
-
-  int arow[GM_A_COPIES];
-#pragma unroll
-  for (int j = 0; j < GM_A_COPIES; ++j) {
-    const int p = P0 + gm_copy_row(wave, lane, j);
-    arow[j] = min(max(row0 + (p - s), 0), T - 1);
-  }
-  f32x16 acc[4][4];
-  gemm_mainloop(acc, smem, X, W, cf.H, n0, arow);
-
+  const int b = tl.b, tloc = tl.tloc, P0 = tl.P0, n0 = tl.n0, mt = tl.mt;
+  const int32_t* rec = tl.rec;
+  const int s = rec[PL_START], e = rec[PL_END];
+  uint8_t* smem = xch;
   const int D = cf.D, cD = COFF * D;
   const float* stg = staging + (size_t)b * COFF * R * 2 * cD;
   const int wfirst = s / R, wend = e / R;             // windows [wfirst, wend) complete
@@ -547,5 +563,53 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
   }
   if (bad) set_error(err, bad);
 }
+
+// Persistent kernel: one workgroup per CU walks its tiles.  Workgroup i runs
+// on XCD i % 8; each XCD takes a contiguous run of tiles (N fastest) and its
+// workgroups take every (workgroups per XCD)-th tile of it, so the XCD's
+// co-running tiles share x rows and panel slices in its L2.  While a tile
+// runs its last three K steps, the next tile's first three stages are copied,
+// so its epilogue overlaps the next tile's pipeline fill.
+template <int R, int COFF>
+__global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
+    Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int T, int B,
+    const int32_t* __restrict__ plan, const int32_t* __restrict__ tile_count,
+    const float* __restrict__ ape, const float* __restrict__ staging,
+    float* __restrict__ kv_state, float* __restrict__ score_state,
+    const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
+    float* __restrict__ pooled, int out_rows, float* __restrict__ split,
+    uint32_t* __restrict__ err) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  uint8_t* xch = smem + GM_LDS_BYTES;
+  const int tiles_n = cf.N / GM_BN;
+  const int total = *tile_count * tiles_n;
+  const int per_wg = gridDim.x >> 3;                // workgroups per XCD
+  const int per_xcd = (total + 7) >> 3;             // tiles per XCD
+  const int lo = (blockIdx.x & 7) * per_xcd;
+  const int hi = min(lo + per_xcd, total);
+  int tile = lo + (blockIdx.x >> 3);
+  if (tile >= hi) return;
+  const size_t ksteps = (size_t)(cf.H >> 4);
+  const int KT = cf.H / GM_BK;
+  PoolTile cur = pool_tile<R>(tile, tiles_n, plan, B);
+  GmSrc csrc = pool_sources(cur, cf, X, W, T);
+  gm_prologue(smem, csrc, ksteps);
+  f32x16 acc[4][4];
+  while (true) {
+    const int next = tile + per_wg;
+    const bool has_next = next < hi;
+    const PoolTile nxt = has_next ? pool_tile<R>(next, tiles_n, plan, B) : cur;
+    const GmSrc nsrc = has_next ? pool_sources(nxt, cf, X, W, T) : csrc;
+    gemm_tile_any(acc, smem, csrc, nsrc, has_next, ksteps, KT);
+    pool_epilogue<R, COFF>(cf, acc, xch, cur, ape, staging, kv_state, score_state, kv_tab,
+                           st_tab, pooled, out_rows, split, err);
+    if (!has_next) break;
+    tile = next;
+    cur = nxt;
+    csrc = nsrc;
+  }
+  gm_drain();
+}
+
 
 }  // namespace cmp

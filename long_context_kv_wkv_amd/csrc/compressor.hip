@@ -181,7 +181,7 @@ constexpr int kDecodeMaxBatch = 64;
 constexpr int kDecodeMaxRows = 64;       // packed x rows of a decode call
 
 struct DecodeLayout {
-  size_t err, partial, pp, ppflag, total;
+  size_t err, partial, pp, ppflag, rec, total;
   int ks, split;
 };
 DecodeLayout decode_layout(const Cfg& cf, int B) {
@@ -193,6 +193,7 @@ DecodeLayout decode_layout(const Cfg& cf, int B) {
   L.partial = o;   o = align256(o + (size_t)L.ks * kDecodeMaxRows * cf.N * 4);
   L.pp = o;        o = align256(o + (size_t)B * DEC_MAX_WIN * L.split * 3 * cf.D * 4);
   L.ppflag = o;    o = align256(o + (size_t)B * DEC_MAX_WIN * L.split * 4);
+  L.rec = o;       o = align256(o + (size_t)(B + 1) * sizeof(DecRec));
   L.total = o;
   return L;
 }
@@ -408,6 +409,7 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
   float* partial = reinterpret_cast<float*>(ws + L.partial);
   float* pp = reinterpret_cast<float*>(ws + L.pp);
   int32_t* ppflag = reinterpret_cast<int32_t*>(ws + L.ppflag);
+  DecRec* rec = reinterpret_cast<DecRec*>(ws + L.rec);
   const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
   const int B = a->batch;
   const int steps = cf.H / 16 / (L.ks * 4);
@@ -426,7 +428,7 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
     });
     hipLaunchKernelGGL(kern, gg, dim3(GV_THREADS), 0, st, cf, X, W, partial, B, T, nwin, steps,
                        a->cu_seqlens, a->seqused, a->start_pos, a->kv_state, a->score_state, kvt,
-                       a->state_block_table, pp, ppflag, err);
+                       a->state_block_table, pp, ppflag, rec, err);
   }));
   return launch("decode_tail", st, [&] {
     const uint16_t* gamma = static_cast<const uint16_t*>(a->norm_weight);
@@ -442,12 +444,17 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
                          a->score_state, kvt, a->state_block_table, pp, ppflag, gamma, cosv,
                          sinv, had, out, a->out_rows, err);
     } else {
-      decltype(&decode_tail1_kernel<4, 2>) tail = nullptr;
-      with_ratio(cf.ratio, [&]<int R>() { tail = decode_tail1_kernel<R, coff_of<R>()>; });
-      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, L.ks, B,
-                         a->seqused, a->start_pos, a->ape, a->kv_state, a->score_state, kvt,
-                         a->state_block_table, pp, ppflag, gamma, cosv, sinv, had, out,
-                         a->out_rows, err);
+      // the tail loads a fixed number of K ranges (>= L.ks, <= DEC_MAX_KSPLIT)
+      decltype(&decode_tail1_kernel<4, 2, 8>) tail = nullptr;
+      with_ratio(cf.ratio, [&]<int R>() {
+        constexpr int C = coff_of<R>();
+        tail = L.ks <= 8 ? decode_tail1_kernel<R, C, 8>
+                         : (L.ks <= 16 ? decode_tail1_kernel<R, C, 16>
+                                       : decode_tail1_kernel<R, C, DEC_MAX_KSPLIT>);
+      });
+      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, L.ks, B, rec,
+                         a->ape, a->kv_state, a->score_state, pp, ppflag, gamma, cosv, sinv, had,
+                         out, a->out_rows, err);
     }
   });
 }

@@ -172,12 +172,66 @@ __device__ __forceinline__ void prepool_block(const Cfg& cf, int b, int k, int s
   if (threadIdx.x == 0) ppflag[(b * DEC_MAX_WIN + k) * NSPLIT + sp] = (int32_t)bad;
 }
 
+// Request record of a single-token call (one row per request), written by
+// the main kernel's first workgroup for the tail: start position, output
+// row, flags and the ring rows of the token's state.  Record B holds the
+// active-request count (s) and the argument-error bits (o).
+enum DecRecFlag { DR_ACT = 1, DR_COMP = 2, DR_STORE = 4, DR_ROW_OK = 8 };
+struct DecRec {
+  int32_t s, o, flags, pad;
+  long rk, rs;
+};
+template <int R, int COFF>
+__device__ __forceinline__ void dec_records(const Cfg& cf, int B, const int32_t* __restrict__ seqused,
+                                            const int32_t* __restrict__ start_pos,
+                                            const int32_t* __restrict__ kv_tab,
+                                            const int32_t* __restrict__ st_tab, DecRec* rec) {
+  const int b = threadIdx.x;                       // one wave, B <= 64
+  const bool in = b < B;
+  const int n = in ? (seqused ? seqused[b] : 1) : 0;
+  const int s = in && start_pos ? start_pos[b] : 0;
+  const bool n_ok = n >= 0 && n <= 1;
+  const bool s_ok = s >= 0 && s <= 0x7fffffff - DEC_MAX_TOK;
+  const bool act = in && n_ok && s_ok && n == 1;
+  const unsigned long long amask = __ballot(act);
+  const uint32_t bad = (__ballot(in && !n_ok) ? CMP_DEVERR_SEQLEN : 0u) |
+                       (__ballot(in && n_ok && !s_ok) ? CMP_DEVERR_START_POS : 0u);
+  if (b == 0) {                                   // record B: count, error bits
+    DecRec t;
+    t.s = __popcll(amask);
+    t.o = (int32_t)bad;
+    t.flags = 0;
+    t.pad = 0;
+    t.rk = 0;
+    t.rs = 0;
+    rec[B] = t;
+  }
+  if (!in) return;
+  const int e = s + 1;
+  // the token's ring row stays live unless the window it closes is the
+  // last one the ring needs (coff 1: a completed window is not kept)
+  const int lo = max(s, R * (e / R) - (COFF - 1) * R);
+  long rk = 0, rs = 0;
+  const bool store = act && lo <= s;
+  const bool row_ok = store && state_row(cf, kv_tab, b, s, &rk) && state_row(cf, st_tab, b, s, &rs);
+  DecRec t;
+  t.s = act ? s : 0;
+  t.o = __popcll(amask & ((1ull << b) - 1ull));
+  t.flags = (act ? DR_ACT : 0) | (act && e % R == 0 ? DR_COMP : 0) | (store ? DR_STORE : 0) |
+            (row_ok ? DR_ROW_OK : 0);
+  t.pad = 0;
+  t.rk = rk;
+  t.rs = rs;
+  rec[b] = t;
+}
+
 // Decode main kernel.  Workgroups [0, B * nwin * split) pre-pool ring windows
 // (prepool_block; nwin <= DEC_MAX_WIN is the most windows a request can
 // complete in this call); the rest run the GEMV over the T packed rows:
 // workgroup g owns column block g % (N / 32) and K range g / (N / 32), its 4
 // waves divide the range, reduce through LDS in a fixed order and write one
-// fp32 partial per K range.
+// fp32 partial per K range.  With one row per request (cu NULL), workgroup 0
+// also writes the request records.
 template <int NRB, int R, int COFF>
 __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
     Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
@@ -186,7 +240,8 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
     const int32_t* __restrict__ start_pos,
     const float* __restrict__ kv_state, const float* __restrict__ score_state,
     const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
-    float* __restrict__ pp, int32_t* __restrict__ ppflag, uint32_t* __restrict__ err) {
+    float* __restrict__ pp, int32_t* __restrict__ ppflag, DecRec* __restrict__ rec,
+    uint32_t* __restrict__ err) {
   // per wave: the x rows of a run, then (after the runs) its accumulators
   constexpr int RUN = 16 / NRB;                  // k-steps per run: 16 KiB of x per wave
   __shared__ __attribute__((aligned(1024))) uint8_t xstage[4][NRB * 32 * RUN * 32];
@@ -194,6 +249,8 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
   const int npre = B * nwin * NSPLIT;
   if ((int)blockIdx.x < npre) {
     const int idx = blockIdx.x;
+    if (idx == 0 && cu == nullptr && threadIdx.x < 64)
+      dec_records<R, COFF>(cf, B, seqused, start_pos, kv_tab, st_tab, rec);
     prepool_block<R, COFF>(cf, idx / (nwin * NSPLIT), (idx / NSPLIT) % nwin,
                            idx % NSPLIT, T, cu, seqused, start_pos, kv_state, score_state, kv_tab,
                            st_tab, pp, ppflag);
@@ -537,15 +594,16 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
 }
 
 // Decode tail for one row per request (no cu_seqlens): the general tail
-// below specialised to a single token, so every load it needs is issued at
-// once (the token's partials, the pre-pooled statistics, the norm weight,
-// rotary values and state tables); same steps and results.
-template <int R, int COFF>
+// above specialised to a single token.  The main kernel has written the
+// request records, so the workgroup's loads take two rounds: its record, the
+// token's K-range partials (KSB >= KS of them, unconditionally: index KS - 1
+// repeats and is not summed), the pre-pooled statistics and the norm weight
+// at once; then Ape and the rotary values, which need the record's position
+// and output row.
+template <int R, int COFF, int KSB>
 __global__ __launch_bounds__(TL_THREADS) void decode_tail1_kernel(
-    Cfg cf, const float* __restrict__ partial, int KS, int B, const int32_t* __restrict__ seqused,
-    const int32_t* __restrict__ start_pos, const float* __restrict__ ape,
-    float* __restrict__ kv_state, float* __restrict__ score_state,
-    const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
+    Cfg cf, const float* __restrict__ partial, int KS, int B, const DecRec* __restrict__ rec,
+    const float* __restrict__ ape, float* __restrict__ kv_state, float* __restrict__ score_state,
     const float* __restrict__ pp, const int32_t* __restrict__ ppflag,
     const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ cosv,
     const uint16_t* __restrict__ sinv, const uint16_t* __restrict__ had, uint16_t* __restrict__ out,
@@ -556,96 +614,77 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail1_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int D = cf.D, cD = COFF * D;
 
-  // active requests (one valid token each) as a 64-bit mask, identical in
-  // every wave; a request with an invalid start position is empty
-  const int sl = lane < B && start_pos ? start_pos[lane] : 0;
-  const bool act = lane < B && (seqused ? seqused[lane] == 1 : true) && sl >= 0 &&
-                   sl <= 0x7fffffff - DEC_MAX_TOK;
-  const unsigned long long amask = __ballot(act);
-  const int total = __popcll(amask);
-
   if ((int)blockIdx.x == B) {                    // rows after the last request's
-    if (total > out_rows && tid == 0) set_error(err, CMP_DEVERR_OUT_ROWS);
+    const DecRec t = rec[B];
+    const int total = t.s;
+    if (tid == 0) set_error(err, (uint32_t)t.o | (total > out_rows ? CMP_DEVERR_OUT_ROWS : 0u));
     for (long i = (long)total * D + tid; i < (long)out_rows * D; i += TL_THREADS) out[i] = 0;
     return;
   }
   const int b = blockIdx.x;
-  const int o = __popcll(amask & ((1ull << b) - 1ull));
-  int n = seqused ? seqused[b] : 1;
-  int s = start_pos ? start_pos[b] : 0;
-  uint32_t bad = 0;
-  if (n < 0 || n > 1) { bad |= CMP_DEVERR_SEQLEN; n = 0; }
-  if (s < 0 || s > 0x7fffffff - DEC_MAX_TOK) { bad |= CMP_DEVERR_START_POS; n = 0; s = 0; }
-  if (bad && tid == 0) set_error(err, bad);
-  if (n == 0) return;
-  if (o >= out_rows) {
-    if (tid == 0) set_error(err, CMP_DEVERR_OUT_ROWS);
-    return;
-  }
-  const int e = s + 1;
-  const bool completing = (e % R) == 0;
   const int c = tid;
   const bool own = c < D;
 
-  // 1. the token's projected values of channel c, and (completing) the
-  //    pre-pooled statistics: every load before the first use
+  // 1. every load that does not depend on the record: the token's K-range
+  //    partials (kv and score of channel c in every channel set), the
+  //    pre-pooled statistics of the window it may close, the norm weight
+  const DecRec rb = rec[b];
   float kvc[COFF], zc[COFF];
   float pm[NSPLIT], pl[NSPLIT], px[NSPLIT];
-#pragma unroll
-  for (int cs = 0; cs < COFF; ++cs) { kvc[cs] = 0.f; zc[cs] = 0.f; }
-  if (own) {
+  const int cl = own ? c : 0;
+  {
     const float* pb = partial + (size_t)b * cf.N;
     const size_t kstride = (size_t)B * cf.N;
-    // all K ranges' loads in flight at once (KS <= DEC_MAX_KSPLIT), summed
-    // in K order
-    float pk[COFF][DEC_MAX_KSPLIT], pz[COFF][DEC_MAX_KSPLIT];
+    float pk[COFF][KSB], pz[COFF][KSB];
 #pragma unroll
     for (int cs = 0; cs < COFF; ++cs) {
-      const int ck = packed_col(0, cs, c, COFF), cz = packed_col(1, cs, c, COFF);
+      const int ck = packed_col(0, cs, cl, COFF), cz = packed_col(1, cs, cl, COFF);
 #pragma unroll
-      for (int ks = 0; ks < DEC_MAX_KSPLIT; ++ks) {
-        pk[cs][ks] = ks < KS ? pb[ks * kstride + ck] : 0.f;
-        pz[cs][ks] = ks < KS ? pb[ks * kstride + cz] : 0.f;
+      for (int ks = 0; ks < KSB; ++ks) {
+        const size_t kk = (size_t)min(ks, KS - 1) * kstride;
+        pk[cs][ks] = pb[kk + ck];
+        pz[cs][ks] = pb[kk + cz];
       }
     }
 #pragma unroll
-    for (int cs = 0; cs < COFF; ++cs) {
-#pragma unroll
-      for (int ks = 0; ks < DEC_MAX_KSPLIT; ++ks) {
-        kvc[cs] += pk[cs][ks];
-        zc[cs] += pz[cs][ks];
-      }
-      zc[cs] += ape[(long)(s % R) * cD + cs * D + c];
+    for (int q = 0; q < NSPLIT; ++q) {
+      const float* st = pp + ((size_t)(b * DEC_MAX_WIN * NSPLIT + q) * 3) * D + cl;
+      pm[q] = st[0];
+      pl[q] = st[D];
+      px[q] = st[2 * D];
     }
-    if (completing) {
 #pragma unroll
-      for (int q = 0; q < NSPLIT; ++q) {
-        const float* st = pp + ((size_t)(b * DEC_MAX_WIN * NSPLIT + q) * 3) * D + c;
-        pm[q] = st[0];
-        pl[q] = st[D];
-        px[q] = st[2 * D];
+    for (int cs = 0; cs < COFF; ++cs) {
+      kvc[cs] = 0.f;
+      zc[cs] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KSB; ++ks) {
+        kvc[cs] += ks < KS ? pk[cs][ks] : 0.f;
+        zc[cs] += ks < KS ? pz[cs][ks] : 0.f;
       }
     }
   }
+  const float g = bf2f(gamma[cl]);
+  if (!(rb.flags & DR_ACT)) return;
+  // 2nd round: Ape of the token's position (score of every channel set)
+#pragma unroll
+  for (int cs = 0; cs < COFF; ++cs) zc[cs] += ape[(long)(rb.s % R) * cD + cs * D + cl];
+  const int o = rb.o;
+  if (o >= out_rows) return;                     // reported by workgroup B
+  const bool completing = (rb.flags & DR_COMP) != 0;
   if (completing && tid < NSPLIT) {
     const int32_t f = ppflag[b * DEC_MAX_WIN * NSPLIT + tid];
     if (f) set_error(err, (uint32_t)f);
   }
-  // loads the later steps need, issued with the ones above: norm weight,
-  // this channel's cos / sin columns, the token's state rows
+  // the rotary values of this channel for output row o
   const int rope0 = D - cf.rope;
   const bool rope_lane = own && c >= rope0;
-  const float g = own ? bf2f(gamma[c]) : 0.f;
   float rc = 0.f, rsn = 0.f;
   if (completing && rope_lane) {
     const int col = ((c - rope0) >> 1) + ((c & 1) ? cf.rope / 2 : 0);
     rc = bf2f(cosv[(size_t)o * cf.rope + col]);
     rsn = bf2f(sinv[(size_t)o * cf.rope + col]);
   }
-  const int lo = max(s, R * (e / R) - (COFF - 1) * R);
-  long rk = 0, rs = 0;
-  const bool store_row = lo <= s;
-  const bool rows_ok = store_row && state_row(cf, kv_tab, b, s, &rk) && state_row(cf, st_tab, b, s, &rs);
 
   if (completing) {
     // 2. pooled value of channel c: the token is the window's last slot
@@ -706,19 +745,17 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail1_kernel(
   }
 
   // 3. the token's state row
-  uint32_t tbad = 0;
-  if (own && store_row) {
-    if (rows_ok) {
+  if (own && (rb.flags & DR_STORE)) {
+    if (rb.flags & DR_ROW_OK) {
 #pragma unroll
       for (int cs = 0; cs < COFF; ++cs) {
-        kv_state[rk * cD + cs * D + c] = kvc[cs];
-        score_state[rs * cD + cs * D + c] = zc[cs];
+        kv_state[rb.rk * cD + cs * D + c] = kvc[cs];
+        score_state[rb.rs * cD + cs * D + c] = zc[cs];
       }
-    } else {
-      tbad |= CMP_DEVERR_TABLE;
+    } else if (c == 0) {
+      set_error(err, CMP_DEVERR_TABLE);
     }
   }
-  if (tbad) set_error(err, tbad);
 }
 
 }  // namespace cmp

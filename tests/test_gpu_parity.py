@@ -235,11 +235,12 @@ def test_determinism_bitwise(harness):
     assert np.array_equal(a, d.out_bits())
 
 
-def test_prefill_equals_token_by_token_decode(harness):
+@pytest.mark.parametrize("rotate", [True, False])
+def test_prefill_equals_token_by_token_decode(harness, rotate):
     """Config-4 style: packed varlen prefill vs the same tokens fed one per
     request per call through the decode entry point, state carried over."""
-    _announce("prefill vs token-by-token decode")
-    w = _varlen_small("varlen_dec", 40, rotate=True, B=6)
+    _announce(f"prefill vs token-by-token decode, rotate={rotate}")
+    w = _varlen_small(f"varlen_dec_{int(rotate)}", 40, rotate=rotate, B=6)
     case = harness.DeviceCase(w)
     case.prefill()
     res = O.compressor(w)

@@ -100,15 +100,15 @@ def test_decode(harness, ratio, emit):
         assert int(res.plan.nwin.sum()) == w["batch"]
 
 
-@pytest.mark.parametrize("ratio", [2, 16])
-def test_prefill_equals_token_by_token_decode(harness, ratio):
+@pytest.mark.parametrize("ratio,rotate", [(2, True), (16, True), (2, False), (32, False)])
+def test_prefill_equals_token_by_token_decode(harness, ratio, rotate):
     """The same tokens through one prefill call and through one decode call
     per token (state carried over): every window's output within the
     tolerance, the live state rows equal within fp32 rounding."""
-    _announce(f"prefill vs decode r={ratio}")
+    _announce(f"prefill vs decode r={ratio} rotate={rotate}")
     spec = _spec(f"ratio{ratio}_stream", ratio, batch=3, lengths=(3 * ratio + 1, 2 * ratio, 5),
                  start_pos=(0, ratio - 1, 1), block_size=8, separate_kv_table=False,
-                 rotate=True)
+                 rotate=rotate)
     w = workloads.build(spec, workloads.SEED_BASE + 360 + ratio)
     case = harness.DeviceCase(w)
     case.prefill()

@@ -437,8 +437,13 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
     const uint16_t* had = static_cast<const uint16_t*>(a->hadamard);
     uint16_t* out = static_cast<uint16_t*>(a->out);
     if (a->cu_seqlens) {
-      decltype(&decode_tail_kernel<4, 2>) tail = nullptr;
-      with_ratio(cf.ratio, [&]<int R>() { tail = decode_tail_kernel<R, coff_of<R>()>; });
+      decltype(&decode_tail_kernel<4, 2, 8>) tail = nullptr;
+      with_ratio(cf.ratio, [&]<int R>() {
+        constexpr int C = coff_of<R>();
+        tail = L.ks <= 8 ? decode_tail_kernel<R, C, 8>
+                         : (L.ks <= 16 ? decode_tail_kernel<R, C, 16>
+                                       : decode_tail_kernel<R, C, DEC_MAX_KSPLIT>);
+      });
       hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, L.ks, B, T,
                          a->cu_seqlens, a->seqused, a->start_pos, a->ape, a->kv_state,
                          a->score_state, kvt, a->state_block_table, pp, ppflag, gamma, cosv,

@@ -319,37 +319,50 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
 // ---------------------------------------------------------------------------
 constexpr int TL_THREADS = 512;
 
-// kv and score (before Ape) of channel c of packed row `row`, in every
-// channel set: the K-range partials, all loads in flight, summed in K order
-template <int COFF>
-__device__ __forceinline__ void dec_token_values(const float* __restrict__ partial, int row, int T,
-                                                 int N, int KS, int c, float (&kv)[COFF],
-                                                 float (&z)[COFF]) {
+// kv and score (before Ape) of channel c of tokens t0 .. t0 + TC - 1 (packed
+// rows row0 + t, t < n), in every channel set: the K-range partials of the
+// TC tokens all in flight at once (KSB >= KS ranges each, unconditionally:
+// indices past the last token or K range repeat it and are not summed),
+// summed in K order.
+template <int COFF, int KSB, int TC>
+__device__ __forceinline__ void dec_token_values(const float* __restrict__ partial, int row0,
+                                                 int t0, int n, int T, int N, int KS, int c,
+                                                 float (&kv)[DEC_MAX_TOK][COFF],
+                                                 float (&z)[DEC_MAX_TOK][COFF]) {
   const size_t kstride = (size_t)T * N;
-  const float* pb = partial + (size_t)row * N;
-  float pk[COFF][DEC_MAX_KSPLIT], pz[COFF][DEC_MAX_KSPLIT];
+  float pk[TC][COFF][KSB], pz[TC][COFF][KSB];
 #pragma unroll
-  for (int cs = 0; cs < COFF; ++cs) {
-    const int ck = packed_col(0, cs, c, COFF), cz = packed_col(1, cs, c, COFF);
+  for (int j = 0; j < TC; ++j) {
+    const float* pb = partial + (size_t)(row0 + min(t0 + j, n - 1)) * N;
 #pragma unroll
-    for (int ks = 0; ks < DEC_MAX_KSPLIT; ++ks) {
-      pk[cs][ks] = ks < KS ? pb[ks * kstride + ck] : 0.f;
-      pz[cs][ks] = ks < KS ? pb[ks * kstride + cz] : 0.f;
+    for (int cs = 0; cs < COFF; ++cs) {
+      const int ck = packed_col(0, cs, c, COFF), cz = packed_col(1, cs, c, COFF);
+#pragma unroll
+      for (int ks = 0; ks < KSB; ++ks) {
+        const size_t kk = (size_t)min(ks, KS - 1) * kstride;
+        pk[j][cs][ks] = pb[kk + ck];
+        pz[j][cs][ks] = pb[kk + cz];
+      }
     }
   }
 #pragma unroll
-  for (int cs = 0; cs < COFF; ++cs) {
-    kv[cs] = 0.f;
-    z[cs] = 0.f;
+  for (int j = 0; j < TC; ++j) {
+    if (t0 + j >= DEC_MAX_TOK) break;
 #pragma unroll
-    for (int ks = 0; ks < DEC_MAX_KSPLIT; ++ks) {
-      kv[cs] += pk[cs][ks];
-      z[cs] += pz[cs][ks];
+    for (int cs = 0; cs < COFF; ++cs) {
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KSB; ++ks) {
+        a += ks < KS ? pk[j][cs][ks] : 0.f;
+        b += ks < KS ? pz[j][cs][ks] : 0.f;
+      }
+      kv[t0 + j][cs] = a;
+      z[t0 + j][cs] = b;
     }
   }
 }
 
-template <int R, int COFF>
+template <int R, int COFF, int KSB>
 __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
     Cfg cf, const float* __restrict__ partial, int KS, int B, int T,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seqused,
@@ -378,7 +391,11 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
   for (int t = 0; t < DEC_MAX_TOK; ++t)
 #pragma unroll
     for (int cs = 0; cs < COFF; ++cs) { kvt[t][cs] = 0.f; zt[t][cs] = 0.f; }
-  if (own && !packed) dec_token_values<COFF>(partial, b, T, cf.N, KS, c, kvt[0], zt[0]);
+  // tokens whose partials are loaded in one round
+  constexpr int TC = (128 / (KSB * 2 * COFF)) < 1 ? 1
+                     : ((128 / (KSB * 2 * COFF)) > DEC_MAX_TOK ? DEC_MAX_TOK
+                                                                : (128 / (KSB * 2 * COFF)));
+  if (own && !packed) dec_token_values<COFF, KSB, 1>(partial, b, 0, 1, T, cf.N, KS, c, kvt, zt);
   float pm0[NSPLIT], pl0[NSPLIT], px0[NSPLIT];
 #pragma unroll
   for (int sp = 0; sp < NSPLIT; ++sp) {
@@ -465,9 +482,9 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
   if (own) {
     if (packed) {
 #pragma unroll
-      for (int t = 0; t < DEC_MAX_TOK; ++t) {
-        if (t >= n) break;
-        dec_token_values<COFF>(partial, q.row0 + t, T, cf.N, KS, c, kvt[t], zt[t]);
+      for (int t0 = 0; t0 < DEC_MAX_TOK; t0 += TC) {
+        if (t0 >= n) break;
+        dec_token_values<COFF, KSB, TC>(partial, q.row0, t0, n, T, cf.N, KS, c, kvt, zt);
       }
     }
 #pragma unroll

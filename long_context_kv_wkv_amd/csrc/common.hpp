@@ -19,16 +19,16 @@ constexpr float kRmsEps = 1e-6f;
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN becomes the quiet NaN 0x7FC0.
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+// fp32 -> bf16 by the hardware conversion (v_cvt_pk_bf16_f32, two values
+// per instruction): round to nearest even; a NaN stays a quiet NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // ---------------------------------------------------------------------------
@@ -93,6 +93,32 @@ __device__ __forceinline__ bool state_row(const Cfg& cf, const int32_t* __restri
   if (blk < 0 || blk >= cf.nblocks) return false;
   *row_index = (long)blk * cf.bs + (q % cf.bs);
   return true;
+}
+
+// v of lane (this lane) ^ M, M a power of two below 64, by register permutes
+// only (no LDS): DPP quad permutes for M = 1, 2, row shifts for 4, a row
+// rotate for 8, v_permlane16_swap / v_permlane32_swap for 16 and 32.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (M == 1) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    const int up = __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, true);          // row_shl:4, from i + 4
+    const int dn = __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, true);          // row_shr:4, from i - 4
+    return __int_as_float((threadIdx.x & 4) ? dn : up);
+  } else if constexpr (M == 8) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true));  // row_ror:8
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(M == 32, "lane_xor: M in 1, 2, 4, ..., 32");
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  }
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

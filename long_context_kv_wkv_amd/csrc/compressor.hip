@@ -139,14 +139,15 @@ int device_cu_count() {
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct PrefillLayout {
-  size_t err, tiles, plan, pooled, hadF, staging, split, total;
+  size_t err, tiles, hadflag, plan, pooled, hadF, staging, split, total;
 };
 int prefill_max_tiles(const Cfg& cf, int T, int B);
 PrefillLayout prefill_layout(const Cfg& cf, int T, int B, int out_rows) {
   PrefillLayout L;
   size_t o = 0;
   L.err = 0;
-  L.tiles = 4;    o += 256;                // error word, then the GEMM tile count
+  L.tiles = 4;                             // error word, GEMM tile count, and
+  L.hadflag = 8;  o += 256;                // "Had is not a scaled Sylvester matrix"
   L.plan = o;     o = align256(o + (size_t)B * PL_WIDTH * 4);
   L.pooled = o;   o = align256(o + (size_t)out_rows * cf.D * 4);
   L.hadF = o;     o = align256(o + (cf.rotate ? (size_t)cf.D * cf.D * 2 : 0));
@@ -336,6 +337,7 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + L.err);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  uint32_t* had_general = reinterpret_cast<uint32_t*>(ws + L.hadflag);
   int32_t* plan = reinterpret_cast<int32_t*>(ws + L.plan);
   float* pooled = reinterpret_cast<float*>(ws + L.pooled);
   uint16_t* hadF = reinterpret_cast<uint16_t*>(ws + L.hadF);
@@ -347,12 +349,12 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
   CMP_TRY(launch("plan", st, [&] {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, a->cu_seqlens,
                        a->seqused, a->start_pos, B, T, cf.ratio, cf.coff, GM_BM, a->out_rows,
-                       plan, tiles, err);
+                       plan, tiles, err, had_general);
   }));
   if (cf.rotate) {
     CMP_TRY(launch("hadamard_pack", st, [&] {
       hipLaunchKernelGGL(hadamard_pack_kernel, dim3(cf.D * cf.D / 8 / 256), dim3(256), 0, st,
-                         static_cast<const uint16_t*>(a->hadamard), hadF, cf.D);
+                         static_cast<const uint16_t*>(a->hadamard), hadF, cf.D, had_general);
     }));
   }
   if (T > 0) {
@@ -384,13 +386,13 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
         hipLaunchKernelGGL(post_kernel<8>, qg, dim3(256), lds, st, cf, pooled, split, plan, B,
                            a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
                            static_cast<const uint16_t*>(a->cos),
-                           static_cast<const uint16_t*>(a->sin), hadF,
+                           static_cast<const uint16_t*>(a->sin), hadF, had_general,
                            static_cast<uint16_t*>(a->out));
       else
         hipLaunchKernelGGL(post_kernel<2>, qg, dim3(256), lds, st, cf, pooled, split, plan, B,
                            a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
                            static_cast<const uint16_t*>(a->cos),
-                           static_cast<const uint16_t*>(a->sin), hadF,
+                           static_cast<const uint16_t*>(a->sin), hadF, had_general,
                            static_cast<uint16_t*>(a->out));
     }));
   }

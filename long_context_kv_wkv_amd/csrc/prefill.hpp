@@ -24,7 +24,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ seqused,
     const int32_t* __restrict__ start_pos, int B, int T, int ratio, int coff, int tile_rows,
     int out_rows, int32_t* __restrict__ plan, int32_t* __restrict__ tile_count,
-    uint32_t* __restrict__ err) {
+    uint32_t* __restrict__ err, uint32_t* __restrict__ had_general) {
   __shared__ int scan[PLAN_THREADS];
   __shared__ int scan2[PLAN_THREADS];
   __shared__ uint32_t s_err;
@@ -91,6 +91,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     if (s_carry > out_rows) e |= CMP_DEVERR_OUT_ROWS;
     *err = e;                                       // this call's error word
     *tile_count = s_tcarry;
+    *had_general = 0;                               // set by hadamard_pack_kernel
   }
 }
 
@@ -124,9 +125,13 @@ __device__ __forceinline__ bool row_has_window(const int32_t* __restrict__ plan,
 // cos/sin column i, the odd one with column 32 + i.
 //
 // Each wave normalises 16 rows in four batches of 4 (all loads of a batch in
-// flight before the first reduction).  The product reads each Had fragment
-// once per workgroup, four k-steps ahead of its use; the result goes back
-// through the LDS tile so that the bf16 rows leave as 16-byte stores.
+// flight before the first reduction).  When Had is a scaled Sylvester matrix
+// (hadamard_pack_kernel leaves *had_general zero) the product is the fast
+// Walsh-Hadamard transform of the fp32 row in registers (log2 D butterfly
+// stages: within a lane, then across lanes), times Had[0][0]: no matrix
+// reads.  Otherwise the MFMA product reads each Had fragment once per
+// workgroup, four k-steps ahead of its use, and the result goes back through
+// the LDS tile so that the bf16 rows leave as 16-byte stores.
 // ---------------------------------------------------------------------------
 constexpr int POST_ROWS = 64;
 constexpr int POST_BATCH = 4;
@@ -145,18 +150,45 @@ __device__ __forceinline__ int post_lds(int lr, int ch) {
   return lr * D * 2 + ((ch ^ (lr & 15)) << 4);
 }
 
+// One butterfly stage of the transform across lanes: lane pairs (l, l ^ M),
+// the lower lane keeping a + b, the upper one a - b (a from the lower lane).
+template <int M, int CPL>
+__device__ __forceinline__ void fwht_lanes(float (&y)[CPL], int lane) {
+  const float sgn = (lane & M) ? -1.f : 1.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) y[i] = fmaf(sgn, y[i], lane_xor<M>(y[i]));
+}
+
 template <int CPL>
 __global__ __launch_bounds__(256) void post_kernel(
     Cfg cf, const float* __restrict__ pooled, const float* __restrict__ split,
     const int32_t* __restrict__ plan, int B, int out_rows,
     const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ cosv,
     const uint16_t* __restrict__ sinv, const uint16_t* __restrict__ hadF,
-    uint16_t* __restrict__ out) {
+    const uint32_t* __restrict__ had_general, uint16_t* __restrict__ out) {
   constexpr int D = CPL * 64;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [64][D] bf16, swizzled
   __shared__ int32_t row_live[POST_ROWS];
+  // per row of the workgroup: bit 0 holds a window, bit 1 a window split
+  // between GEMM tiles, bits 2.. that window's second tile
+  __shared__ int32_t row_info[POST_ROWS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row_base = blockIdx.x * POST_ROWS;
+  if ((int)threadIdx.x < POST_ROWS) {             // every row's plan lookup at once
+    const int row = row_base + threadIdx.x;
+    int info = 0;
+    const int rb = row < out_rows ? find_request(plan, B, row) : -1;
+    if (rb >= 0) {
+      const int32_t* rrec = plan + (long)rb * PL_WIDTH;
+      const int k = row - rrec[PL_OUT0];
+      if (k < rrec[PL_NWIN]) {
+        info = 1;
+        if (cf.coff == 2 && k > 0 && (k & 63) == 0) info |= 2 | ((rrec[PL_TILE0] + (k >> 6)) << 2);
+      }
+    }
+    row_info[threadIdx.x] = info;
+  }
+  __syncthreads();
   const int c0 = lane * CPL;
   const int rope0 = D - cf.rope, half = cf.rope / 2;
   const bool rope_lane = c0 >= rope0;
@@ -164,6 +196,8 @@ __global__ __launch_bounds__(256) void post_kernel(
   float g[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) g[i] = bf2f(gamma[c0 + i]);
+  const bool fwht = cf.rotate && *had_general == 0;
+  const float hscale = cf.rotate ? bf2f(hadF[0]) : 0.f;   // Had[0][0]
 
 #pragma unroll 1
   for (int bt = 0; bt < POST_ROWS / 4 / POST_BATCH; ++bt) {
@@ -194,15 +228,12 @@ __global__ __launch_bounds__(256) void post_kernel(
     float ss[POST_BATCH];
 #pragma unroll
     for (int q = 0; q < POST_BATCH; ++q) {
-      const int row = row_base + lr0 + q;
-      const int rb = row < out_rows ? find_request(plan, B, row) : -1;
-      const int32_t* rrec = plan + (long)(rb < 0 ? 0 : rb) * PL_WIDTH;
-      const int k = row - rrec[PL_OUT0];
-      live[q] = rb >= 0 && k < rrec[PL_NWIN];
-      if (live[q] && cf.coff == 2 && k > 0 && (k & 63) == 0) {
+      const int info = row_info[lr0 + q];
+      live[q] = (info & 1) != 0;
+      if (info & 2) {
         // a window split between two GEMM tiles: first channel set from the
         // previous tile, second set from this one
-        const int mt = rrec[PL_TILE0] + (k >> 6);
+        const int mt = info >> 2;
         const float* pa = split + (size_t)(mt - 1) * 6 * D + c0;
         const float* pb = split + (size_t)mt * 6 * D + 3 * D + c0;
 #pragma unroll
@@ -226,9 +257,14 @@ __global__ __launch_bounds__(256) void post_kernel(
       ss[q] = acc;
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-#pragma unroll
-      for (int q = 0; q < POST_BATCH; ++q) ss[q] += __shfl_xor(ss[q], off, 64);
+    for (int q = 0; q < POST_BATCH; ++q) {
+      ss[q] += lane_xor<32>(ss[q]);
+      ss[q] += lane_xor<16>(ss[q]);
+      ss[q] += lane_xor<8>(ss[q]);
+      ss[q] += lane_xor<4>(ss[q]);
+      ss[q] += lane_xor<2>(ss[q]);
+      ss[q] += lane_xor<1>(ss[q]);
+    }
 #pragma unroll
     for (int q = 0; q < POST_BATCH; ++q) {
       const int lr = lr0 + q;
@@ -243,10 +279,31 @@ __global__ __launch_bounds__(256) void post_kernel(
           y[q][i + 1] = o * bf2f(rt[q][1].v[i / 2]) + e * bf2f(rt[q][3].v[i / 2]);
         }
       }
+      if (fwht) {
+        // y . Had = Had[0][0] * WHT(y): butterflies over channel bit b, bits
+        // below log2(CPL) inside the lane, the others against lane ^ 2^j
+#pragma unroll
+        for (int h = 1; h < CPL; h <<= 1)
+#pragma unroll
+          for (int i = 0; i < CPL; ++i)
+            if ((i & h) == 0) {
+              const float a = y[q][i], b = y[q][i + h];
+              y[q][i] = a + b;
+              y[q][i + h] = a - b;
+            }
+        fwht_lanes<1>(y[q], lane);
+        fwht_lanes<2>(y[q], lane);
+        fwht_lanes<4>(y[q], lane);
+        fwht_lanes<8>(y[q], lane);
+        fwht_lanes<16>(y[q], lane);
+        fwht_lanes<32>(y[q], lane);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) y[q][i] *= hscale;
+      }
       uint32_t pk[CPL / 2];
 #pragma unroll
       for (int i = 0; i < CPL; i += 2) pk[i / 2] = live[q] ? pack_bf2(y[q][i], y[q][i + 1]) : 0u;
-      if (cf.rotate) {
+      if (cf.rotate && !fwht) {
         if constexpr (CPL == 8)
           *reinterpret_cast<uint4*>(smem + post_lds<D>(lr, lane)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         else
@@ -261,7 +318,7 @@ __global__ __launch_bounds__(256) void post_kernel(
       }
     }
   }
-  if (!cf.rotate) return;
+  if (!cf.rotate || fwht) return;
   __syncthreads();
 
   // out[64, D] = Y[64, D] . Had; wave w owns output columns [w*D/4, (w+1)*D/4)
@@ -332,20 +389,32 @@ __global__ __launch_bounds__(256) void post_kernel(
 // Had (D x D bf16, row k, column n) in the fragment-major order of the MFMA B
 // operand: fragment (column block cb, k-step kk) is 64 lanes x 8 values, lane
 // l holding column cb*32 + l%32 and rows kk*16 + 8*(l/32) .. +8.  One thread
-// per lane piece; D*D/8 pieces.
+// per lane piece; D*D/8 pieces.  The same pass checks whether Had is the
+// Sylvester matrix times a constant, Had[k][n] = Had[0][0] * (-1)^popcount(k & n)
+// bit for bit, with Had[0][0] finite and non-zero; any other matrix sets
+// *had_general (cleared by plan_kernel), and post_kernel then multiplies by
+// the matrix instead of running the fast transform.
 __global__ __launch_bounds__(256) void hadamard_pack_kernel(const uint16_t* __restrict__ had,
-                                                            uint16_t* __restrict__ hadF, int D) {
+                                                            uint16_t* __restrict__ hadF, int D,
+                                                            uint32_t* __restrict__ had_general) {
   const int o = blockIdx.x * 256 + threadIdx.x;
   if (o >= D * D / 8) return;
   const int lane = o & 63, f = o >> 6;
   const int ks = D / 16;
   const int cb = f / ks, kk = f - cb * ks;
   const int n = cb * 32 + (lane & 31), k0 = kk * 16 + 8 * (lane >> 5);
+  const uint32_t h00 = had[0];
+  bool sylvester = (h00 & 0x7FFFu) != 0 && (h00 & 0x7F80u) != 0x7F80u;
   uint32_t v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = had[(size_t)(k0 + e) * D + n];
+  for (int e = 0; e < 8; ++e) {
+    v[e] = had[(size_t)(k0 + e) * D + n];
+    const uint32_t want = (__popc((uint32_t)((k0 + e) & n)) & 1) ? (h00 ^ 0x8000u) : h00;
+    sylvester = sylvester && v[e] == want;
+  }
   *reinterpret_cast<uint4*>(hadF + (size_t)o * 8) =
       make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+  if (__ballot(!sylvester) && lane == 0) atomicOr(had_general, 1u);
 }
 
 // ---------------------------------------------------------------------------

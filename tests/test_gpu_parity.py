@@ -89,6 +89,29 @@ def test_varlen_reduced(harness, max_len, pad):
     assert case.device_error() == 0
 
 
+@pytest.mark.parametrize("kind", ["random", "one_entry_flipped", "sylvester_times_minus_2"])
+def test_prefill_hadamard_matrix_kinds(harness, kind):
+    """The rotation matrix is an input: a scaled Sylvester matrix (any sign
+    or scale) takes the in-register transform, anything else the matrix
+    product; both against the oracle's plain product with the same matrix."""
+    _announce(f"prefill with a {kind} rotation matrix")
+    w = _varlen_small(f"varlen_had_{kind}", 300, rotate=True, B=3)
+    D = w["head_dim"]
+    syl = workloads.bf16_bits_to_f32(w["hadamard"])
+    if kind == "random":
+        rng = np.random.default_rng(workloads.SEED_BASE + 91)
+        m = (rng.standard_normal((D, D)) / np.sqrt(D)).astype(np.float32)
+    elif kind == "one_entry_flipped":
+        m = syl.copy()
+        m[D // 2 + 3, 5] = -m[D // 2 + 3, 5]
+    else:
+        m = syl * np.float32(-2.0)
+    w = dict(w, hadamard=workloads.f32_to_bf16_bits(m))
+    case, res = _run_prefill(harness, w)
+    assert_out(case.out_bits(), res)
+    assert case.device_error() == 0
+
+
 def test_varlen_full_sampled(harness):
     _announce("varlen_c4a full size, sampled rows")
     w = workloads.build_named("varlen_c4a")

@@ -46,8 +46,16 @@ __global__ __launch_bounds__(NSA_THREADS) void nsa_compress_kernel(
     const int32_t* __restrict__ table, int B, int table_stride, int num_blocks, long T,
     uint16_t* __restrict__ out, long result_len, uint32_t* __restrict__ err) {
   __shared__ long s_cu;
+  __shared__ int32_t s_tab[NSA_THREADS];
   const int b = blockIdx.x;
   const long E = (long)cf.N * cf.D;
+  // a table row of at most NSA_THREADS entries is read whole, together with
+  // the batch's length and slot, so that the page lookup below is no second
+  // dependent round trip
+  const bool tab_lds = cf.paged && table_stride <= NSA_THREADS;
+  if (tab_lds && (int)threadIdx.x < table_stride)
+    s_tab[threadIdx.x] = table[(long)b * table_stride + threadIdx.x];
+  const int slot = slot_mapping[b];
   const long s = act[b];
   uint32_t bad = 0;
   if (s < 0) bad |= NSA_DEVERR_SEQLEN;
@@ -62,13 +70,14 @@ __global__ __launch_bounds__(NSA_THREADS) void nsa_compress_kernel(
     if (part) atomicAdd(reinterpret_cast<unsigned long long*>(&s_cu), (unsigned long long)part);
     __syncthreads();
     cu = s_cu;
+  } else if (tab_lds) {
+    __syncthreads();
   }
   const long e0 = ((long)blockIdx.y * NSA_THREADS + threadIdx.x) * NSA_PER_THREAD;
   if (!fires || bad) {
     if (bad && threadIdx.x == 0 && blockIdx.y == 0 && err) atomicOr(err, bad);
     return;
   }
-  const int slot = slot_mapping[b];
   if (slot < 0 || slot >= result_len) bad |= NSA_DEVERR_SLOT;
   const long first = s - CBS;                    // compressIdx * stride
   long base0 = 0, base1 = 0;                     // element offsets of the window's pages
@@ -79,8 +88,8 @@ __global__ __launch_bounds__(NSA_THREADS) void nsa_compress_kernel(
     if (page1 >= table_stride) {
       bad |= NSA_DEVERR_TABLE;
     } else {
-      const int b0 = table[(long)b * table_stride + page0];
-      const int b1 = table[(long)b * table_stride + page1];
+      const int b0 = tab_lds ? s_tab[page0] : table[(long)b * table_stride + page0];
+      const int b1 = tab_lds ? s_tab[page1] : table[(long)b * table_stride + page1];
       if (b0 < 0 || b0 >= num_blocks || b1 < 0 || b1 >= num_blocks) bad |= NSA_DEVERR_TABLE;
       base0 = (long)b0 * cf.page * E;
       base1 = (long)b1 * cf.page * E;

@@ -65,6 +65,32 @@ def test_prefill_varlen_continuation(harness, ratio):
     print(f"r={ratio}: max scaled err {mx:.2e}, MAE {mae:.2e}")
 
 
+@pytest.mark.parametrize("ratio,batch", [(4, 33), (4, 64), (128, 64)])
+def test_decode_more_than_32_requests(harness, ratio, batch):
+    """One token per request with 33..64 requests (the 64-row GEMV): every
+    other request closes a window, every fifth is inactive (seqused 0), so
+    output rows are packed over the active ones."""
+    _announce(f"decode r={ratio} batch={batch}")
+    spec = _spec(f"ratio{ratio}_decode_b{batch}", ratio, hidden=2048, batch=batch, lengths=(1,),
+                 start_pos=("uniform", 0, 65535), block_size=64, separate_kv_table=False,
+                 out_rows=batch)
+    w = workloads.build(spec, workloads.SEED_BASE + 380 + ratio + batch)
+    sp = w["start_pos"].astype(np.int64)
+    sp[::2] = sp[::2] - sp[::2] % ratio + ratio - 1
+    used = np.ones(batch, np.int32)
+    used[::5] = 0
+    w = dict(w, start_pos=sp.astype(np.int32), seqused=used)
+    case = harness.DeviceCase(w)
+    case.decode()
+    torch.cuda.synchronize()
+    res = O.compressor(w)
+    assert_out(case.out_bits(), res)
+    kv, sc = case.states()
+    assert_states(kv, sc, w, res)
+    assert case.device_error() == 0
+    assert int(res.plan.nwin.sum()) == int(np.sum(used * ((sp + 1) % ratio == 0)))
+
+
 @pytest.mark.parametrize("ratio", [2, 16])
 def test_prefill_aligned_long_and_padded(harness, ratio):
     """Window-aligned starts and long requests (interior tiles, no prefix),

@@ -168,7 +168,7 @@ int prefill_max_tiles(const Cfg& cf, int T, int B) {
 // stream the panel; each wave's share is a whole number of 8-step (128-k) runs
 int decode_ksplit(const Cfg& cf) {
   const int cblocks = cf.N / 32;
-  const int units = cf.H / 512;             // 128-k runs per wave x 4 waves
+  const int units = cf.H / (128 * (GV_THREADS / 64));   // 8-step runs per wave x 8 waves
   int best = 1;
   for (int ks = 1; ks <= units; ++ks) {
     if (units % ks) continue;
@@ -414,7 +414,7 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
   DecRec* rec = reinterpret_cast<DecRec*>(ws + L.rec);
   const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
   const int B = a->batch;
-  const int steps = cf.H / 16 / (L.ks * 4);
+  const int steps = cf.H / 16 / (L.ks * (GV_THREADS / 64));
   const int T = a->T;
   // the most windows a request can complete: its tokens (one without
   // cu_seqlens, else at most 4 and at most T) span ceil(tokens / ratio)

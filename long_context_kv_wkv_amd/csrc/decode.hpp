@@ -3,9 +3,9 @@
 // The projection of B <= 64 tokens streams the whole weight panel from HBM
 // once, so it is bound by HBM bandwidth, not by the matrix cores.  It is split
 // over output columns and K so that every CU streams its own slice: a
-// workgroup owns 32 panel columns and one K range that its 4 waves divide;
+// workgroup owns 32 panel columns and one K range that its 8 waves divide;
 // each wave multiplies its x fragments (rows = tokens) by the weight
-// fragments it loads straight from HBM with the 32x32x16 bf16 MFMA.  The 4
+// fragments it loads straight from HBM with the 32x32x16 bf16 MFMA.  The 8
 // waves reduce through LDS and the workgroup writes one fp32 partial per K
 // range; the tail kernel sums the K ranges in a fixed order (deterministic).
 //
@@ -17,7 +17,7 @@
 
 namespace cmp {
 
-constexpr int GV_THREADS = 256;
+constexpr int GV_THREADS = 512;                // 8 waves
 
 typedef __attribute__((address_space(3))) void dec_lds_t;
 typedef __attribute__((address_space(1))) void dec_glb_t;
@@ -27,8 +27,9 @@ typedef __attribute__((address_space(1))) void dec_glb_t;
 // runs of rows (a row of the run is U*32 contiguous bytes), then the panel
 // fragments of the run are loaded (1 KiB contiguous each); once the copies
 // have landed, the x fragments are read from LDS and the MFMAs run.  Row t,
-// chunk c sits at t*U*32 + ((c ^ (t & 15)) * 16): the fragment reads (32
-// rows at one chunk index) are bank conflict free.  Rows >= B repeat row
+// chunk c sits at t*U*32 + ((c ^ (t & m)) * 16), m = min(2U, 16) - 1 (the
+// swizzle never leaves the row's 2U chunks): the fragment reads (32 rows at
+// one chunk index) spread over the banks.  Rows >= B repeat row
 // B-1 (their results are not used).
 template <int U, int NRB>
 __device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp,
@@ -36,11 +37,13 @@ __device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp,
                                          uint8_t* xl, f32x16* acc) {
   constexpr int CPR = 2 * U;             // 16-byte chunks per row of the run
   constexpr int RPI = 64 / CPR;          // rows per copy instruction
+  constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;   // chunk swizzle mask: stays inside the row
+  static_assert(U >= 1 && U <= 32 && (U & (U - 1)) == 0, "run length: a power of two");
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < NRB * U; ++j) {
     const int t = j * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ (t & 15);
+    const int c = (lane % CPR) ^ (t & SWZ);
     __builtin_amdgcn_global_load_lds((dec_glb_t*)(xk + (size_t)min(t, B - 1) * K + s * 16 + c * 8),
                                      (dec_lds_t*)(xl + j * 1024), 16, 0, 0);
   }
@@ -57,7 +60,7 @@ __device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp,
     for (int rb = 0; rb < NRB; ++rb) {
       const int t = rb * 32 + (lane & 31);
       const int c = 2 * u + (lane >> 5);
-      const bf16x8 xf = *reinterpret_cast<const bf16x8*>(xl + t * CPR * 16 + ((c ^ (t & 15)) << 4));
+      const bf16x8 xf = *reinterpret_cast<const bf16x8*>(xl + t * CPR * 16 + ((c ^ (t & SWZ)) << 4));
       acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, wf[u], acc[rb], 0, 0, 0);
     }
   // the next run's copies overwrite the region: every read must be done
@@ -228,7 +231,7 @@ __device__ __forceinline__ void dec_records(const Cfg& cf, int B, const int32_t*
 // Decode main kernel.  Workgroups [0, B * nwin * split) pre-pool ring windows
 // (prepool_block; nwin <= DEC_MAX_WIN is the most windows a request can
 // complete in this call); the rest run the GEMV over the T packed rows:
-// workgroup g owns column block g % (N / 32) and K range g / (N / 32), its 4
+// workgroup g owns column block g % (N / 32) and K range g / (N / 32), its 8
 // waves divide the range, reduce through LDS in a fixed order and write one
 // fp32 partial per K range.  With one row per request (cu NULL), workgroup 0
 // also writes the request records.
@@ -243,8 +246,8 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
     float* __restrict__ pp, int32_t* __restrict__ ppflag, DecRec* __restrict__ rec,
     uint32_t* __restrict__ err) {
   // per wave: the x rows of a run, then (after the runs) its accumulators
-  constexpr int RUN = 16 / NRB;                  // k-steps per run: 16 KiB of x per wave
-  __shared__ __attribute__((aligned(1024))) uint8_t xstage[4][NRB * 32 * RUN * 32];
+  constexpr int RUN = 8 / NRB;                   // k-steps per run: 8 KiB of x per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t xstage[GV_THREADS / 64][NRB * 32 * RUN * 32];
   constexpr int NSPLIT = dec_split<R>();
   const int npre = B * nwin * NSPLIT;
   if ((int)blockIdx.x < npre) {
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (g == 0 && tid == 0) *err = 0;   // this call's error word (only the tail sets bits)
   if (T == 0) return;
-  const int kstep0 = (kr * 4 + wave) * steps_per_wave;
+  const int kstep0 = (kr * (GV_THREADS / 64) + wave) * steps_per_wave;
   // fragment (column block cb, k-step kstep0 + u) is 1 KiB contiguous
   const uint16_t* wp = W + (((size_t)cb * (K >> 4) + kstep0) * 64 + lane) * 8;
   const uint16_t* xk = X + (size_t)kstep0 * 16;
@@ -278,21 +281,18 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
   int s = 0;
   // (every wave's share is a multiple of 8 k-steps)
   for (; s + RUN <= steps_per_wave; s += RUN) gemv_run<RUN, NRB>(wp, xk, K, T, s, xl, acc);
-  if constexpr (RUN > 8) {
-    if (s < steps_per_wave) gemv_run<8, NRB>(wp, xk, K, T, s, xl, acc);
-  }
   float* red = reinterpret_cast<float*>(xl);            // [NRB * 16][64] of this wave
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[(rb * 16 + r) * 64 + lane] = acc[rb][r];
   __syncthreads();
-  // fixed-order sum of the 4 waves; element (reg, lane) -> (row, column)
+  // fixed-order sum of the 8 waves; element (reg, lane) -> (row, column)
   for (int e = tid; e < NRB * 16 * 64; e += GV_THREADS) {
     const int reg = e >> 6, ln = e & 63;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) v += reinterpret_cast<const float*>(xstage[w])[reg * 64 + ln];
+    for (int w = 0; w < GV_THREADS / 64; ++w) v += reinterpret_cast<const float*>(xstage[w])[reg * 64 + ln];
     const int rb = reg >> 4, r = reg & 15;
     const int row = rb * 32 + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
     const int col = cb * 32 + (ln & 31);

@@ -1,4 +1,4 @@
-// Decode kernels: one token per request.
+// Decode kernels: at most 4 tokens per request, at most 64 packed rows.
 //
 // The projection of B <= 64 tokens streams the whole weight panel from HBM
 // once, so it is bound by HBM bandwidth, not by the matrix cores.  It is split

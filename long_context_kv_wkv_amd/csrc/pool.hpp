@@ -238,40 +238,29 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
         }
   } else {
     // R >= 8: wave window w holds blocks i and runs rg with
-    // (32 i + 8 rg) / R == w, in both lane halves
+    // (32 i + 8 rg) / R == w, in both lane halves.  One pass of online
+    // statistics per channel, one 32-row block at a time (each block's loads
+    // fenced below the previous block's), so few values are live at once.
     constexpr int NW = 128 / R;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      Soft st[2];
+      Soft st[2] = {Soft{-INFINITY, 0.f, 0.f}, Soft{-INFINITY, 0.f, 0.f}};
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        float m = -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        if ((32 * i + 31) / R < w || (32 * i) / R > w) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int r = 0; r < 16; ++r) {
+          if ((32 * i + 8 * (r >> 2)) / R != w) continue;
+          const int jr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if ((32 * i + 8 * (r >> 2)) / R != w) continue;
-            const int jr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+          for (int ch = 0; ch < 2; ++ch) {
             float kv, z;
-            if (epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r], jr, ch ? t.c1 : t.c0, kv, z))
-              m = fmaxf(m, z);
+            if (epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r], jr,
+                                   ch ? t.c1 : t.c0, kv, z))
+              soft_add(st[ch], z, kv);
           }
-        st[ch] = Soft{m, 0.f, 0.f};
-        if (m != -INFINITY) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              if ((32 * i + 8 * (r >> 2)) / R != w) continue;
-              const int jr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-              float kv, z;
-              if (epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r], jr, ch ? t.c1 : t.c0, kv, z)) {
-                const float pe = __builtin_amdgcn_exp2f((z - m) * kLog2e);
-                st[ch].l += pe;
-                st[ch].x = fmaf(pe, kv, st[ch].x);
-              }
-            }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       // the low half needs the high half's c0 rows, the high half the low
       // half's c1 rows

@@ -238,9 +238,10 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
         }
   } else {
     // R >= 8: wave window w holds blocks i and runs rg with
-    // (32 i + 8 rg) / R == w, in both lane halves.  One pass of online
-    // statistics per channel, one 32-row block at a time (each block's loads
-    // fenced below the previous block's), so few values are live at once.
+    // (32 i + 8 rg) / R == w, in both lane halves.  Statistics one 32-row
+    // block at a time (max, then exponentials, of the block's rows in this
+    // lane), merged into the window's; each block's loads are fenced below
+    // the previous block's, so few values are live at once.
     constexpr int NW = 128 / R;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -248,17 +249,34 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if ((32 * i + 31) / R < w || (32 * i) / R > w) continue;
+        float kvb[2][16], zb[2][16];
+        bool okb[2][16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if ((32 * i + 8 * (r >> 2)) / R != w) continue;
           const int jr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+          const bool inw = (32 * i + 8 * (r >> 2)) / R == w;
 #pragma unroll
           for (int ch = 0; ch < 2; ++ch) {
-            float kv, z;
-            if (epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r], jr,
-                                   ch ? t.c1 : t.c0, kv, z))
-              soft_add(st[ch], z, kv);
+            okb[ch][r] = inw && epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r],
+                                                   jr, ch ? t.c1 : t.c0, kvb[ch][r], zb[ch][r]);
           }
+        }
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+          float m = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) if (okb[ch][r]) m = fmaxf(m, zb[ch][r]);
+          Soft blk{m, 0.f, 0.f};
+          if (m != -INFINITY) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              if (!okb[ch][r]) continue;
+              const float pe = __builtin_amdgcn_exp2f((zb[ch][r] - m) * kLog2e);
+              blk.l += pe;
+              blk.x = fmaf(pe, kvb[ch][r], blk.x);
+            }
+          }
+          st[ch] = soft_merge(st[ch], blk);
         }
         __builtin_amdgcn_sched_barrier(0);
       }

@@ -89,13 +89,21 @@ def test_varlen_reduced(harness, max_len, pad):
     assert case.device_error() == 0
 
 
+@pytest.mark.parametrize("D", [512, 128])
 @pytest.mark.parametrize("kind", ["random", "one_entry_flipped", "sylvester_times_minus_2"])
-def test_prefill_hadamard_matrix_kinds(harness, kind):
+def test_prefill_hadamard_matrix_kinds(harness, kind, D):
     """The rotation matrix is an input: a scaled Sylvester matrix (any sign
     or scale) takes the in-register transform, anything else the matrix
     product; both against the oracle's plain product with the same matrix."""
-    _announce(f"prefill with a {kind} rotation matrix")
-    w = _varlen_small(f"varlen_had_{kind}", 300, rotate=True, B=3)
+    _announce(f"prefill with a {kind} rotation matrix, D={D}")
+    if D == 512:
+        w = _varlen_small(f"varlen_had_{kind}", 300, rotate=True, B=3)
+    else:
+        # the indexer shape (D = 128) from position 2: every request closes a window
+        spec = dataclasses.replace(workloads.P1_COMP_INDEXER, name=f"indexer_had_{kind}",
+                                   start_pos=(2,))
+        w = workloads.build(spec, workloads.SEED_BASE + 93)
+    assert w["head_dim"] == D
     D = w["head_dim"]
     syl = workloads.bf16_bits_to_f32(w["hadamard"])
     if kind == "random":

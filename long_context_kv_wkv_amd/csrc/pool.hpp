@@ -302,7 +302,9 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
   }
 }
 
-constexpr int POOL_LDS_BYTES = GM_LDS_BYTES + 1024;   // copy ring + epilogue exchange
+// The copy ring takes all of LDS; the epilogue's 1 KiB exchange sits in the
+// panel stage that is idle between two tiles (GM_IDLE_OFF).
+constexpr int POOL_LDS_BYTES = GM_LDS_BYTES;
 
 // One tile of a request: M-tile mt (its request b, the tile's first position
 // P0 and its index tloc among the request's tiles) and N-tile nt.
@@ -337,11 +339,11 @@ __device__ __forceinline__ GmSrc pool_sources(const PoolTile& t, const Cfg& cf,
     const int p = t.P0 + gm_copy_row(wave, lane, j);
     arow[j] = min(max(row0 + (p - s), 0), T - 1);
   }
-  return gm_sources(X, W, cf.H, t.n0, arow);
+  return gm_sources(X, W, cf.H, t.n0, arow, min(max(row0 + (t.P0 - s), 0), T - 1));
 }
 
 // Pooling epilogue of one tile (see the top of this file).  xch: 1 KiB of LDS
-// outside the copy ring.
+// that no copy fills and no K loop reads while the epilogue runs.
 template <int R, int COFF>
 __device__ __forceinline__ void pool_epilogue(
     const Cfg& cf, const f32x16 (&acc)[4][4], uint8_t* xch, const PoolTile& tl,
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
     float* __restrict__ pooled, int out_rows, float* __restrict__ split,
     uint32_t* __restrict__ err) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  uint8_t* xch = smem + GM_LDS_BYTES;
+  uint8_t* xch = smem + GM_IDLE_OFF;
   const int tiles_n = cf.N / GM_BN;
   const int total = *tile_count * tiles_n;
   const int per_wg = gridDim.x >> 3;                // workgroups per XCD
@@ -596,24 +598,33 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
   const int hi = min(lo + per_xcd, total);
   int tile = lo + (blockIdx.x >> 3);
   if (tile >= hi) return;
-  const size_t ksteps = (size_t)(cf.H >> 4);
+  const int ksteps = cf.H >> 4;
   const int KT = cf.H / GM_BK;
   PoolTile cur = pool_tile<R>(tile, tiles_n, plan, B);
   GmSrc csrc = pool_sources(cur, cf, X, W, T);
   gm_prologue(smem, csrc, ksteps);
   f32x16 acc[4][4];
+  const int xstep = (KT >> 1) % 3;   // X buffer rotation per tile
+  int xrot = 0;
   while (true) {
     const int next = tile + per_wg;
     const bool has_next = next < hi;
     const PoolTile nxt = has_next ? pool_tile<R>(next, tiles_n, plan, B) : cur;
     const GmSrc nsrc = has_next ? pool_sources(nxt, cf, X, W, T) : csrc;
-    gemm_tile_any(acc, smem, csrc, nsrc, has_next, ksteps, KT);
+    gemm_tile_any(acc, smem, csrc, nsrc, has_next, ksteps, KT, xrot);
     pool_epilogue<R, COFF>(cf, acc, xch, cur, ape, staging, kv_state, score_state, kv_tab,
                            st_tab, pooled, out_rows, split, err);
     if (!has_next) break;
     tile = next;
     cur = nxt;
-    csrc = nsrc;
+    // rebuild the copy sources rather than carry them through the epilogue,
+    // whose register demand would spill them (an opaque tile field keeps the
+    // compiler from reusing the values computed before the K loop)
+    cur.P0 = __builtin_amdgcn_readfirstlane(cur.P0);
+    asm volatile("" : "+s"(cur.P0));
+    csrc = pool_sources(cur, cf, X, W, T);
+    xrot += xstep;
+    if (xrot >= 3) xrot -= 3;
   }
   gm_drain();
 }

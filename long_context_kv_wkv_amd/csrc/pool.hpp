@@ -317,8 +317,11 @@ template <int R>
 __device__ __forceinline__ PoolTile pool_tile(int tile, int tiles_n, const int32_t* __restrict__ plan,
                                               int B) {
   PoolTile t;
-  t.mt = tile / tiles_n;
-  t.nt = tile - t.mt * tiles_n;
+  // tiles_n = N / 256 = coff * D / 128 is a power of two (D is 128 or 512):
+  // a shift keeps the tile walk in scalar registers, so the plan lookups
+  // below are scalar loads that do not wait on the copies in flight
+  t.mt = tile >> __builtin_ctz(tiles_n);
+  t.nt = tile & (tiles_n - 1);
   t.b = find_tile_request(plan, B, t.mt);
   t.rec = plan + (long)t.b * PL_WIDTH;
   t.tloc = t.mt - t.rec[PL_TILE0];

@@ -4,11 +4,15 @@
 // step 1; [AscendC] 具体计算流程 矩阵乘法), both weight matrices in one panel so
 // a single pass over X produces every projected column.
 //
-// Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2, each wave a
-// 128 x 128 sub-tile = 4 x 4 blocks of the 32x32x16 bf16 MFMA, accumulators
-// in AGPRs), K step 32, operands staged in LDS by direct-to-LDS copies
-// (global_load_lds_dwordx4: no staging registers, no ds_write), all 160 KiB
-// of the CU's LDS:
+// Tiling: 256 x 256 output tile per workgroup of 8 waves, two per SIMD (4 x
+// 2, each wave a 64 x 128 sub-tile = 2 x 4 blocks of the 32x32x16 bf16 MFMA,
+// 128 accumulator registers).  With one wave per SIMD (128 x 128 sub-tiles)
+// a wave that waits for the load unit to accept a copy leaves the SIMD's
+// matrix core idle; with two, the other wave's MFMAs fill that time (3%
+// faster at the 128K C4A shape, although every wave now reads half of a
+// fragment set it shares with three others).  K step 32, operands staged in
+// LDS by direct-to-LDS copies (global_load_lds_dwordx4: no staging
+// registers, no ds_write), all 160 KiB of the CU's LDS:
 //  * X: three 32 KiB buffers, each two K steps (256 rows x 128 B), so every
 //    copy fetches whole 128-byte cache lines (8 rows x 128 B per copy
 //    instruction).  Rows are row-major with their 16-byte chunks
@@ -20,7 +24,7 @@
 // Copies run three K steps ahead of the MFMAs (the X buffers: two to four):
 // on MI355X one step of MFMA work (~0.5 us) is shorter than the latency of a
 // batch of copies (~1.2 us measured), so fewer stages leave the MFMAs
-// waiting.  The 8 copies of a step are interleaved one per two MFMAs.
+// waiting.  Each wave issues 4 copies per step, one per four MFMAs.
 //
 // Workgroups are persistent (one per CU, each walking a run of tiles): the
 // last three K steps of a tile issue the copies of the first three steps of
@@ -38,16 +42,19 @@
 namespace cmp {
 
 constexpr int GM_BM = 256, GM_BN = 256, GM_BK = 32;
-constexpr int GM_THREADS = 256;
+constexpr int GM_WAVES = 8;
+constexpr int GM_THREADS = 64 * GM_WAVES;
+constexpr int GM_WROWS = 64;                                   // rows of a wave's sub-tile
 constexpr int GM_W_STAGE_BYTES = GM_BN * GM_BK * 2;            // 16 KiB
 constexpr int GM_X_BUF_BYTES = GM_BM * 2 * GM_BK * 2;          // 32 KiB: two K steps
 constexpr int GM_X_OFF = 4 * GM_W_STAGE_BYTES;                 // panel stages first
 constexpr int GM_LDS_BYTES = GM_X_OFF + 3 * GM_X_BUF_BYTES;    // 160 KiB
-constexpr int GM_A_COPIES = GM_BM * 2 * GM_BK * 2 / 1024 / 4;  // X copies per wave and buffer (8)
+constexpr int GM_A_COPIES = GM_X_BUF_BYTES / 1024 / GM_WAVES;  // X copies per wave and buffer (4)
 constexpr int GM_A_ROWS = 1024 / (2 * GM_BK * 2);              // X rows per copy instruction (8)
 // LDS the epilogue may use between two tiles: the panel stage of a tile's
 // last K step, which nothing reads or fills until the next tile's first step.
 constexpr int GM_IDLE_OFF = 3 * GM_W_STAGE_BYTES;
+constexpr int GM_IDLE_BYTES = GM_W_STAGE_BYTES;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -56,10 +63,6 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)l, 16, 0, 0);
 }
 __device__ __forceinline__ int swz_bits(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-// byte offset of 16-byte chunk `chunk` of row `row` in a 128-byte-row buffer
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return (row << 7) + ((chunk ^ swz_bits(row)) << 4);
-}
 // Tile row that X copy instruction j of `wave` fills for `lane`.
 __device__ __forceinline__ int gm_copy_row(int wave, int lane, int j) {
   return (wave * GM_A_COPIES + j) * GM_A_ROWS + (lane >> 3);
@@ -67,32 +70,32 @@ __device__ __forceinline__ int gm_copy_row(int wave, int lane, int j) {
 
 // ---------------------------------------------------------------------------
 // K loop of one 256 x 256 tile: acc[i][j] (wave (wm, wn), 32x32 block i of
-// its 128 rows, block j of its 128 columns) = X[rows] . Wp[n0 .. n0+256)^T.
+// its 64 rows, block j of its 128 columns) = X[rows] . Wp[n0 .. n0+256)^T.
 // K % 128 == 0 (so the K step count is a multiple of the 4 panel stages).
 //
-// Schedule of a K step (32 MFMAs per wave in 8 groups of 4): each group
-// issues one copy and two LDS fragment reads.  The first half's MFMAs use
-// k-step 0 of the step while k-step 1 is read, the second half's use k-step 1
-// while the next step's k-step 0 is read, and the single barrier of the step
-// sits between the halves, so no LDS read latency is exposed.  The first
-// half issues 4 X copies (half of the buffer two K-step pairs ahead: step
-// 2c issues the first half of pair c+2, step 2c+1 the second), the second
-// half the 4 panel copies of step kt+3.  The copy unit takes a 1 KiB copy
-// every few tens of cycles and a wave cannot issue past a copy it has not
-// accepted, so the waves place their copy at different MFMAs of the group
-// (wave w after MFMA w): copies from the lock-stepped waves reach the unit
-// one after another instead of together.  Every group is fenced so the
-// compiler keeps this order.
+// Schedule of a K step (8 MFMAs per wave and k-step, in 4 groups of 2): each
+// group reads the next k-step's panel fragment (and, in two of them, its X
+// fragment).  The first half's MFMAs use k-step 0 of the step while k-step
+// 1 is read, the second half's use k-step 1 while the next step's k-step 0
+// is read, and the single barrier of the step sits between the halves, so
+// no LDS read latency is exposed.  The first half issues 2 X copies (a
+// quarter of the buffer two K-step pairs ahead: step 2c issues the first
+// half of pair c+2, step 2c+1 the second), the second half the 2 panel
+// copies of step kt+3 (wave w copies column block w of the tile).  The copy
+// unit takes a 1 KiB copy every few tens of cycles and a wave cannot issue
+// past a copy it has not accepted, so the four waves of a SIMD pair place
+// their copies at different MFMAs (P = wave % 4).  Every group is fenced so
+// the compiler keeps this order.
 // ---------------------------------------------------------------------------
 #define GM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | 0x0f70)
-// s_waitcnt vmcnt(12) lgkmcnt(0)
-#define GM_WAIT_VM12_LGKM0() __builtin_amdgcn_s_waitcnt((12 & 0xf) | ((12 >> 4) << 14) | 0x0070)
+// s_waitcnt vmcnt(6) lgkmcnt(0)
+#define GM_WAIT_VM6_LGKM0() __builtin_amdgcn_s_waitcnt(6 | 0x0070)
 #define GM_BARRIER() asm volatile("s_barrier" ::: "memory")
 
 // Copy sources of one tile: a uniform base for X (the tile's first row) and
-// one for the wave's panel fragments, and this lane's byte offsets from them
-// (the copies take the scalar-base address form, so the bases live in scalar
-// registers).
+// one for the wave's panel column block, and this lane's byte offsets from
+// the X base (the copies take the scalar-base address form, so the bases
+// live in scalar registers).
 struct GmSrc {
   const uint8_t* x;
   const uint8_t* w;
@@ -108,7 +111,7 @@ __device__ __forceinline__ GmSrc gm_sources(const uint16_t* __restrict__ X,
                                             const int (&arow)[GM_A_COPIES], int arow0) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   GmSrc src;
-  // X copies: instruction j of wave w fills buffer rows r0 = (8w + j) * 8 ..
+  // X copies: instruction j of wave w fills buffer rows r0 = (4w + j) * 8 ..
   // +8; lane l lands at LDS byte r0*128 + 16 l, i.e. row r0 + l/8, physical
   // chunk l%8, so it fetches the logical chunk the swizzle places there.
 #pragma unroll
@@ -118,49 +121,47 @@ __device__ __forceinline__ GmSrc gm_sources(const uint16_t* __restrict__ X,
     src.a[j] = (uint32_t)(((size_t)(arow[j] - arow0) * K + kc * 8) * 2);
   }
   src.x = reinterpret_cast<const uint8_t*>(X + (size_t)__builtin_amdgcn_readfirstlane(arow0) * K);
-  // panel copies: fragment f = 4w + j of a stage is (column block f / 2,
-  // k-step f % 2); lane offsets come from gm_woff
+  // panel copies: wave w copies column block w (fragments (w, k-step) of a
+  // stage); lane offsets come from gm_woff
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  src.w = reinterpret_cast<const uint8_t*>(
-      W + (((size_t)(n0 >> 5) + 2 * wv) * (size_t)(K >> 4)) * 512);
+  src.w = reinterpret_cast<const uint8_t*>(W + (((size_t)(n0 >> 5) + wv) * (size_t)(K >> 4)) * 512);
   return src;
 }
 
 __device__ __forceinline__ uint8_t* gm_xbuf(uint8_t* smem, int buf) {
   return smem + GM_X_OFF + buf * GM_X_BUF_BYTES;
 }
-// Half h of the X copies of K-step pair c into buffer xb.
-__device__ __forceinline__ void gm_xcopy(const GmSrc& src, int c, int h, uint8_t* xb) {
+// Byte offset of k-step g of K step t in a column block of the panel.
+__device__ __forceinline__ uint32_t gm_woff(int g, int t) {
+  return (uint32_t)(((t * 2 + g) << 10) + (threadIdx.x & 63) * 16);
+}
+// Quarter q of the X copies of K-step pair c into buffer xb.
+__device__ __forceinline__ void gm_xcopy(const GmSrc& src, int c, int q, uint8_t* xb) {
   const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
-    dma16(src.x + (src.a[4 * h + g] + (uint32_t)c * (4 * GM_BK)),
-          xb + (wave * GM_A_COPIES + 4 * h + g) * 1024);
-}
-// Byte offset of panel copy g of K step t from GmSrc::w (a wave's two
-// column blocks are ksteps fragments of 1 KiB each apart).
-__device__ __forceinline__ uint32_t gm_woff(int g, int t, int ksteps) {
-  return (uint32_t)((((g >> 1) * ksteps + t * 2 + (g & 1)) << 10) + (threadIdx.x & 63) * 16);
+  for (int g = 0; g < 2; ++g)
+    dma16(src.x + (src.a[2 * q + g] + (uint32_t)c * (4 * GM_BK)),
+          xb + (wave * GM_A_COPIES + 2 * q + g) * 1024);
 }
 // The panel copies of K step t into stage st.
-__device__ __forceinline__ void gm_wcopy(const GmSrc& src, int t, uint8_t* st, int ksteps) {
+__device__ __forceinline__ void gm_wcopy(const GmSrc& src, int t, uint8_t* st) {
   const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) dma16(src.w + gm_woff(g, t, ksteps), st + (wave * 4 + g) * 1024);
+  for (int g = 0; g < 2; ++g) dma16(src.w + gm_woff(g, t), st + (wave * 2 + g) * 1024);
 }
 
 // The copies of steps 0 .. 2 of a workgroup's first tile (pairs 0 and 1 into
 // X buffers 0 and 1, steps 0 .. 2 into panel stages 0 .. 2), in the order the
 // steady state issues them; later tiles get theirs from the previous tile's
 // last steps.
-__device__ __forceinline__ void gm_prologue(uint8_t* smem, const GmSrc& src, int ksteps) {
+__device__ __forceinline__ void gm_prologue(uint8_t* smem, const GmSrc& src) {
   gm_xcopy(src, 0, 0, gm_xbuf(smem, 0));
   gm_xcopy(src, 0, 1, gm_xbuf(smem, 0));
-  gm_wcopy(src, 0, smem, ksteps);
+  gm_wcopy(src, 0, smem);
   gm_xcopy(src, 1, 0, gm_xbuf(smem, 1));
-  gm_wcopy(src, 1, smem + GM_W_STAGE_BYTES, ksteps);
+  gm_wcopy(src, 1, smem + GM_W_STAGE_BYTES);
   gm_xcopy(src, 1, 1, gm_xbuf(smem, 1));
-  gm_wcopy(src, 2, smem + 2 * GM_W_STAGE_BYTES, ksteps);
+  gm_wcopy(src, 2, smem + 2 * GM_W_STAGE_BYTES);
 }
 
 // The K loop of one tile; xrot = X buffer of its K-step pair 0.  Step kt
@@ -171,38 +172,38 @@ __device__ __forceinline__ void gm_prologue(uint8_t* smem, const GmSrc& src, int
 // keeps the panel stage of step kt at kt % 4 in every tile; the X buffers
 // continue their rotation into the next tile.
 template <int P>
-__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], uint8_t* smem, const GmSrc& cur,
-                                          const GmSrc& nxt, bool has_next, int ksteps,
-                                          int KT, int xrot) {
+__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[2][4], uint8_t* smem, const GmSrc& cur,
+                                          const GmSrc& nxt, bool has_next, int KT, int xrot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int KC = KT >> 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // step 0's stage and pair 0 have landed once at most the 16 newest memory
+  // step 0's stage and pair 0 have landed once at most the 8 newest memory
   // operations are outstanding (copies of pair 1 and steps 1 and 2, or the
   // previous epilogue's stores, which come after them)
-  GM_WAIT_VM(16);
+  GM_WAIT_VM(8);
   GM_BARRIER();
   // X buffers of pairs kc, kc + 1, kc + 2
   int xb0 = xrot, xb1 = xrot == 2 ? 0 : xrot + 1, xb2 = xrot == 0 ? 2 : xrot - 1;
-  // this lane's A fragment row (block 0) and its swizzle; block g adds g*4096
-  const int arow_off = (wm * 128 + lrow) << 7;
+  // this lane's A fragment row (block 0) and its swizzle; block i adds i*4096
+  const int arow_off = (wm * GM_WROWS + lrow) << 7;
   const int asw = swz_bits(lrow);
   // Fragments: a0/b0 = k-step 0 of the current step, a1/b1 = k-step 1.
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  bf16x8 a0[2], b0[4], a1[2], b1[4];
   {
     const uint8_t* xa = gm_xbuf(smem, xb0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i)
       a0[i] = *reinterpret_cast<const bf16x8*>(xa + arow_off + ((lhalf ^ asw) << 4) + i * 4096);
-      b0[i] = *reinterpret_cast<const bf16x8*>(smem + ((wn * 4 + i) * 2) * 1024 + lane * 16);
-    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b0[j] = *reinterpret_cast<const bf16x8*>(smem + ((wn * 4 + j) * 2) * 1024 + lane * 16);
   }
   for (int kc = 0; kc < KC; ++kc) {
     const uint8_t* xa = gm_xbuf(smem, xb0);
@@ -232,40 +233,41 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], uint8_t* smem, co
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         __builtin_amdgcn_sched_barrier(0);
-        a1[g] = *reinterpret_cast<const bf16x8*>(xa + arow_off + q1 + g * 4096);
         b1[g] = *reinterpret_cast<const bf16x8*>(sb + ((wn * 4 + g) * 2 + 1) * 1024 + lane * 16);
+        if (g < 2) a1[g] = *reinterpret_cast<const bf16x8*>(xa + arow_off + q1 + g * 4096);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j == P) {
+        for (int i = 0; i < 2; ++i) {
+          if ((g & 1) == (P >> 1) && i == (P & 1)) {
             __builtin_amdgcn_sched_barrier(0);
-            dma16(xs.x + (xs.a[4 * p + g] + (uint32_t)xkn * (4 * GM_BK)),
-                  xc + (wave * GM_A_COPIES + 4 * p + g) * 1024);
+            const int j = 2 * p + (g >> 1);
+            dma16(xs.x + (xs.a[j] + (uint32_t)xkn * (4 * GM_BK)),
+                  xc + (wave * GM_A_COPIES + j) * 1024);
             __builtin_amdgcn_sched_barrier(0);
           }
-          acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[g], b0[j], acc[g][j], 0, 0, 0);
+          acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[g], acc[i][g], 0, 0, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
       // step kt+1's panel stage and X pair: this wave's copies are done when
-      // only the 12 issued after them (step kt-1's and the first half of step
+      // only the 6 issued after them (step kt-1's and the first half of step
       // kt's) are outstanding, and the barrier publishes every wave's (a bare
       // barrier: a workgroup fence would wait for every copy)
-      GM_WAIT_VM12_LGKM0();
+      GM_WAIT_VM6_LGKM0();
       GM_BARRIER();
       // second half: panel copies, reads of the next a0/b0, MFMAs of a1 x b1
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         __builtin_amdgcn_sched_barrier(0);
-        a0[g] = *reinterpret_cast<const bf16x8*>(na + arow_off + qn + g * 4096);
         b0[g] = *reinterpret_cast<const bf16x8*>(nb + ((wn * 4 + g) * 2) * 1024 + lane * 16);
+        if (g < 2) a0[g] = *reinterpret_cast<const bf16x8*>(na + arow_off + qn + g * 4096);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j == P) {
+        for (int i = 0; i < 2; ++i) {
+          if ((g & 1) == (P >> 1) && i == (P & 1)) {
             __builtin_amdgcn_sched_barrier(0);
-            dma16(bk + gm_woff(g, kn, ksteps), st + (wave * 4 + g) * 1024);
+            dma16(bk + gm_woff(g >> 1, kn), st + (wave * 2 + (g >> 1)) * 1024);
             __builtin_amdgcn_sched_barrier(0);
           }
-          acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[g], b1[j], acc[g][j], 0, 0, 0);
+          acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[g], acc[i][g], 0, 0, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -278,14 +280,14 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], uint8_t* smem, co
 }
 
 // One tile's K loop with the wave's copy position (see the schedule above).
-__device__ __forceinline__ void gemm_tile_any(f32x16 (&acc)[4][4], uint8_t* smem,
+__device__ __forceinline__ void gemm_tile_any(f32x16 (&acc)[2][4], uint8_t* smem,
                                               const GmSrc& cur, const GmSrc& nxt, bool has_next,
-                                              int ksteps, int KT, int xrot) {
-  switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-    case 0: gemm_tile<0>(acc, smem, cur, nxt, has_next, ksteps, KT, xrot); break;
-    case 1: gemm_tile<1>(acc, smem, cur, nxt, has_next, ksteps, KT, xrot); break;
-    case 2: gemm_tile<2>(acc, smem, cur, nxt, has_next, ksteps, KT, xrot); break;
-    default: gemm_tile<3>(acc, smem, cur, nxt, has_next, ksteps, KT, xrot); break;
+                                              int KT, int xrot) {
+  switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
+    case 0: gemm_tile<0>(acc, smem, cur, nxt, has_next, KT, xrot); break;
+    case 1: gemm_tile<1>(acc, smem, cur, nxt, has_next, KT, xrot); break;
+    case 2: gemm_tile<2>(acc, smem, cur, nxt, has_next, KT, xrot); break;
+    default: gemm_tile<3>(acc, smem, cur, nxt, has_next, KT, xrot); break;
   }
 }
 
@@ -297,7 +299,7 @@ __device__ __forceinline__ void gm_drain() {
 }
 
 #undef GM_WAIT_VM
-#undef GM_WAIT_VM12_LGKM0
+#undef GM_WAIT_VM6_LGKM0
 #undef GM_BARRIER
 
 }  // namespace cmp

@@ -12,14 +12,14 @@
 // first-set statistics of its last window, and the post kernel merges the
 // two halves of each split window (no halo recomputation, no tile waits).
 //
-// Epilogue: the accumulators of wave (wm, wn) hold 128 rows x 128 panel
+// Epilogue: the accumulators of wave (wm, wn) hold 64 rows x 128 panel
 // columns; the panel's column order puts every variant (kv / score, channel
 // set) of a channel in one lane (packed_col), and a lane's rows come in runs
 // of 4 consecutive rows.  So each lane forms, per channel, the softmax
 // statistics (running max m, sum l, weighted sum x) of its window slots,
-// merges them with the statistics its neighbour lane (or, once per tile, the
-// other row-wave) holds for the rest of the window, and writes the pooled
-// value ([CANN] 计算公式 steps 3-5).  Scores get Ape first ([CANN] step 2).
+// merges them with the statistics its neighbour lane (or, at a row-wave
+// boundary, the previous row-wave, through LDS) holds for the rest of the
+// window, and writes the pooled value ([CANN] 计算公式 steps 3-5).  Scores get Ape first ([CANN] step 2).
 // The same epilogue stores the state rows that stay live after the call
 // (positions [max(s, r*floor(e/r) - (coff-1)*r), e)): the GEMM never reads
 // the pool, so there is no read/write hazard inside the kernel.
@@ -143,13 +143,15 @@ __device__ __forceinline__ void store_state(const Cfg& cf, float* __restrict__ k
 
 // ---------------------------------------------------------------------------
 // coff = 1 epilogue (ratios 2, 8, 16, ..., 128): the windows of a row-wave's
-// 128 rows.  Register r of block i holds wave row 32 i + 8 (r / 4) + 4 h + r % 4
+// 64 rows.  Register r of block i holds wave row 32 i + 8 (r / 4) + 4 h + r % 4
 // (h = lane / 32), so a window of R <= 4 rows lies in one lane (R = 4: one
 // run of 4 rows, R = 2: half a run), and a window of R >= 8 rows is split
 // between the two lane halves: each half takes the statistics of its rows
 // (max first, then the exponentials), one cross-half swap merges them, and
-// the low half writes channel c0, the high half c1.  FAST: every row is a
-// token of this call and every window complete (no per-row tests).
+// the low half writes channel c0, the high half c1.  A window of 128 rows
+// spans two row-waves: the odd one hands its statistics to the even one
+// through LDS.  FAST: every row is a token of this call and every window
+// complete (no per-row tests).
 // ---------------------------------------------------------------------------
 struct EpiCtx {
   const Cfg& cf;
@@ -162,6 +164,8 @@ struct EpiCtx {
   int wfirst, wend, wg0;
   int out_rows;
   float* pooled;
+  uint8_t* xch;        // LDS for the two row-waves of a 128-row window
+  int wm, wn;
 };
 
 // value of channel c of (kv or score) at wave row jr: accumulator, Ape, or
@@ -170,9 +174,12 @@ template <int R, bool FAST>
 __device__ __forceinline__ bool epi_value(const EpiCtx& t, float a_kv, float a_z, int jr, int c,
                                           float& kv, float& z) {
   const int cD = t.cf.D;
+  // slot of the row in its window (the wave starts a window unless a window
+  // spans two row-waves)
+  const int q = (R > GM_WROWS ? t.base + jr : jr) & (R - 1);
   if (FAST) {
     kv = a_kv;
-    z = a_z + t.ape[(jr % R) * cD + c];
+    z = a_z + t.ape[q * cD + c];
     return true;
   }
   const int p = t.base + jr;
@@ -183,7 +190,7 @@ __device__ __forceinline__ bool epi_value(const EpiCtx& t, float a_kv, float a_z
     z = row[cD + c];
   } else {
     kv = a_kv;
-    z = a_z + t.ape[(jr % R) * cD + c];
+    z = a_z + t.ape[q * cD + c];
   }
   return z != -INFINITY;
 }
@@ -197,13 +204,13 @@ __device__ __forceinline__ void epi_store(const EpiCtx& t, int wl, int c, const 
 }
 
 template <int R, bool FAST>
-__device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&acc)[2][4]) {
   const int h = t.h;
   if constexpr (R <= 4) {
     // windows inside one lane: R = 4 -> (i, run), R = 2 -> (i, run, pair)
     constexpr int PER_RUN = 4 / R;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg)
 #pragma unroll
@@ -242,12 +249,12 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
     // block at a time (max, then exponentials, of the block's rows in this
     // lane), merged into the window's; each block's loads are fenced below
     // the previous block's, so few values are live at once.
-    constexpr int NW = 128 / R;
+    constexpr int NW = R <= GM_WROWS ? GM_WROWS / R : 1;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       Soft st[2] = {Soft{-INFINITY, 0.f, 0.f}, Soft{-INFINITY, 0.f, 0.f}};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i) {
         if ((32 * i + 31) / R < w || (32 * i) / R > w) continue;
         float kvb[2][16], zb[2][16];
         bool okb[2][16];
@@ -297,7 +304,15 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
         tot.l += other.l * sc;
         tot.x += other.x * sc;
       }
-      epi_store(t, w, h ? t.c1 : t.c0, tot);
+      if constexpr (R > GM_WROWS) {
+        // second half of the window in the odd row-wave of the pair
+        Soft* xs = reinterpret_cast<Soft*>(t.xch) + ((t.wm >> 1) * 2 + t.wn) * 64 + (threadIdx.x & 63);
+        if (t.wm & 1) *xs = tot;
+        __syncthreads();
+        if (!(t.wm & 1)) epi_store(t, w, h ? t.c1 : t.c0, soft_merge(tot, *xs));
+      } else {
+        epi_store(t, w, h ? t.c1 : t.c0, tot);
+      }
     }
   }
 }
@@ -345,11 +360,11 @@ __device__ __forceinline__ GmSrc pool_sources(const PoolTile& t, const Cfg& cf,
   return gm_sources(X, W, cf.H, t.n0, arow, min(max(row0 + (t.P0 - s), 0), T - 1));
 }
 
-// Pooling epilogue of one tile (see the top of this file).  xch: 1 KiB of LDS
-// that no copy fills and no K loop reads while the epilogue runs.
+// Pooling epilogue of one tile (see the top of this file).  xch: LDS (at most
+// 3 KiB used) that no copy fills and no K loop reads while the epilogue runs.
 template <int R, int COFF>
 __device__ __forceinline__ void pool_epilogue(
-    const Cfg& cf, const f32x16 (&acc)[4][4], uint8_t* xch, const PoolTile& tl,
+    const Cfg& cf, const f32x16 (&acc)[2][4], uint8_t* xch, const PoolTile& tl,
     const float* __restrict__ ape, const float* __restrict__ staging,
     float* __restrict__ kv_state, float* __restrict__ score_state,
     const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
@@ -382,9 +397,9 @@ __device__ __forceinline__ void pool_epilogue(
       // Interior tile: every row is a token of this call, no state row is
       // stored, window 0 is split and every other window is complete.  Group
       // statistics in two passes (max, then exp) with no per-row tests.
-      Soft sa[16];
+      Soft sa[8];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
+      for (int t = 0; t < 8; ++t) {
         const int i = t >> 2, r0 = 4 * (t & 3);
         float z[4], v[4];
 #pragma unroll
@@ -394,20 +409,20 @@ __device__ __forceinline__ void pool_epilogue(
         }
         sa[t] = soft_group4(z, v);
       }
-      // window 32 (first of row-wave 1) needs window 31 from row-wave 0
-      Soft* xch = reinterpret_cast<Soft*>(smem);
-      if (wm == 0 && h == 1) xch[wn * 32 + lrow] = sa[15];
+      // the first window of row-wave wm > 0 needs the last window of wm - 1
+      Soft* xch = reinterpret_cast<Soft*>(smem);   // [wm][wn][32 lanes]
+      if (wm < 3 && h == 1) xch[(wm * 2 + wn) * 32 + lrow] = sa[7];
       __syncthreads();
-      const Soft from_wave0 = xch[wn * 32 + lrow];
+      const Soft from_prev = xch[(max(wm - 1, 0) * 2 + wn) * 32 + lrow];
       float* sp = split + (size_t)mt * 6 * D;
-      if (wm == 1 && h == 1) {
-        sp[0 * D + c] = sa[15].m;
-        sp[1 * D + c] = sa[15].l;
-        sp[2 * D + c] = sa[15].x;
+      if (wm == 3 && h == 1) {
+        sp[0 * D + c] = sa[7].m;
+        sp[1 * D + c] = sa[7].l;
+        sp[2 * D + c] = sa[7].x;
       }
-      const int row_base = o + (P0 >> 2) + wm * 32 + h - wfirst;   // output row of slot 0
+      const int row_base = o + (P0 >> 2) + wm * 16 + h - wfirst;   // output row of slot 0
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
+      for (int t = 0; t < 8; ++t) {
         const int i = t >> 2, r0 = 4 * (t & 3);
         float z[4], v[4];
 #pragma unroll
@@ -419,7 +434,7 @@ __device__ __forceinline__ void pool_epilogue(
         // first-set statistics of window w-1: window 2t-1 (low half) sits in
         // the high half at slot t-1, window 2t (high half) in the low half at
         // slot t
-        const Soft& pa = sa[(t + 15) & 15];
+        const Soft& pa = sa[(t + 7) & 7];
         Soft prev{cross_half(pa.m, sa[t].m, h), cross_half(pa.l, sa[t].l, h),
                   cross_half(pa.x, sa[t].x, h)};
         if (t == 0 && h == 0 && wm == 0) {
@@ -427,7 +442,7 @@ __device__ __forceinline__ void pool_epilogue(
           sp[4 * D + c] = sb.l;
           sp[5 * D + c] = sb.x;
         } else {
-          if (t == 0 && h == 0) prev = from_wave0;
+          if (t == 0 && h == 0) prev = from_prev;
           const int row = row_base + 2 * t;
           if (row < out_rows) pooled[(size_t)row * D + c] = soft_value2(prev, sb);
         }
@@ -452,14 +467,14 @@ __device__ __forceinline__ void pool_epilogue(
       return true;
     };
     // statistics of the first channel set per window this lane holds:
-    // window index in the tile w = wm*32 + 8 i + 2 i' + h, rows 4w .. 4w+3
-    Soft sa[4][4];
+    // window index in the tile w = wm*16 + 8 i + 2 i' + h, rows 4w .. 4w+3
+    Soft sa[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int ip = 0; ip < 4; ++ip) {
         Soft st{-INFINITY, 0.f, 0.f};
-        const int w = wm * 32 + 8 * i + 2 * ip + h;
+        const int w = wm * 16 + 8 * i + 2 * ip + h;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float kv[2], z[2];
@@ -467,11 +482,11 @@ __device__ __forceinline__ void pool_epilogue(
         }
         sa[i][ip] = st;
       }
-    // window 32 (first of row-wave 1) needs window 31 from row-wave 0
-    Soft* xch = reinterpret_cast<Soft*>(smem);       // [wn][32 lanes]
-    if (wm == 0 && h == 1) xch[wn * 32 + lrow] = sa[3][3];
+    // the first window of row-wave wm > 0 needs the last window of wm - 1
+    Soft* xch = reinterpret_cast<Soft*>(smem);       // [wm][wn][32 lanes]
+    if (wm < 3 && h == 1) xch[(wm * 2 + wn) * 32 + lrow] = sa[1][3];
     __syncthreads();
-    const Soft from_wave0 = xch[wn * 32 + lrow];
+    const Soft from_prev = xch[(max(wm - 1, 0) * 2 + wn) * 32 + lrow];
     // first-set statistics of the window before the tile: staged state rows
     // (or padding) in the request's first tile, else the previous tile's
     Soft before{-INFINITY, 0.f, 0.f};
@@ -489,27 +504,27 @@ __device__ __forceinline__ void pool_epilogue(
     // split-window statistics of this tile: [mt][a = last window's first
     // set | b = first window's second set][m, l, x][D]
     float* sp = split + (size_t)mt * 6 * D;
-    if (wm == 1 && h == 1) {
-      sp[0 * D + c] = sa[3][3].m;
-      sp[1 * D + c] = sa[3][3].l;
-      sp[2 * D + c] = sa[3][3].x;
+    if (wm == 3 && h == 1) {
+      sp[0 * D + c] = sa[1][3].m;
+      sp[1 * D + c] = sa[1][3].l;
+      sp[2 * D + c] = sa[1][3].x;
     }
     // the other lane half's statistics (every lane takes part in the shuffle)
-    Soft other[4][4];
+    Soft other[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int ip = 0; ip < 4; ++ip) other[i][ip] = soft_shfl_xor(sa[i][ip], 32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int ip = 0; ip < 4; ++ip) {
-        const int w = wm * 32 + 8 * i + 2 * ip + h;
+        const int w = wm * 16 + 8 * i + 2 * ip + h;
         // first-set statistics of window w-1: odd windows (h = 1) find it in
         // the partner lane at the same slot, even ones one slot earlier
         const Soft prev = h == 1 ? other[i][ip]
                                  : (ip > 0 ? other[i][ip - 1]
-                                           : (i > 0 ? other[i - 1][3] : (wm == 1 ? from_wave0 : before)));
+                                           : (i > 0 ? other[i - 1][3] : (wm > 0 ? from_prev : before)));
         // second set of window w, then the pooled value
         Soft sb{-INFINITY, 0.f, 0.f};
 #pragma unroll
@@ -541,21 +556,22 @@ __device__ __forceinline__ void pool_epilogue(
     // 1: score) and c1 (blocks 2, 3) ----
     const int g = (n0 + wn * 128) >> 7;
     const int c0 = g * 64 + lrow, c1 = c0 + 32;
-    EpiCtx ctx{cf, P0 + 128 * wm, s, e, live_lo, rec[PL_FIRST], stg, ape, c0, c1, h,
-               o + (P0 + 128 * wm) / R - wfirst, wfirst, wend, (P0 + 128 * wm) / R,
-               out_rows, pooled};
+    const int wbase = P0 + GM_WROWS * wm;   // position of the wave's first row
+    EpiCtx ctx{cf, wbase, s, e, live_lo, rec[PL_FIRST], stg, ape, c0, c1, h,
+               o + wbase / R - wfirst, wfirst, wend, wbase / R,
+               out_rows, pooled, smem, wm, wn};
     if (P0 >= s && P0 + GM_BM <= live_lo) {
       epilogue_coff1<R, true>(ctx, acc);
     } else {
       epilogue_coff1<R, false>(ctx, acc);
       // state rows that stay live (only a request's last tile has any)
-      if (P0 + 128 * wm + 127 >= live_lo && P0 + 128 * wm < e) {
+      if (wbase + GM_WROWS - 1 >= live_lo && wbase < e) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int jr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);   // row in the wave
-            const int p = P0 + 128 * wm + jr;
+            const int p = wbase + jr;
             if (p >= live_lo && p < e) {
               long rk, rs;
               if (state_row(cf, kv_tab, b, p, &rk) && state_row(cf, st_tab, b, p, &rs)) {
@@ -601,12 +617,11 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
   const int hi = min(lo + per_xcd, total);
   int tile = lo + (blockIdx.x >> 3);
   if (tile >= hi) return;
-  const int ksteps = cf.H >> 4;
   const int KT = cf.H / GM_BK;
   PoolTile cur = pool_tile<R>(tile, tiles_n, plan, B);
   GmSrc csrc = pool_sources(cur, cf, X, W, T);
-  gm_prologue(smem, csrc, ksteps);
-  f32x16 acc[4][4];
+  gm_prologue(smem, csrc);
+  f32x16 acc[2][4];
   const int xstep = (KT >> 1) % 3;   // X buffer rotation per tile
   int xrot = 0;
   while (true) {
@@ -614,7 +629,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
     const bool has_next = next < hi;
     const PoolTile nxt = has_next ? pool_tile<R>(next, tiles_n, plan, B) : cur;
     const GmSrc nsrc = has_next ? pool_sources(nxt, cf, X, W, T) : csrc;
-    gemm_tile_any(acc, smem, csrc, nsrc, has_next, ksteps, KT, xrot);
+    gemm_tile_any(acc, smem, csrc, nsrc, has_next, KT, xrot);
     pool_epilogue<R, COFF>(cf, acc, xch, cur, ape, staging, kv_state, score_state, kv_tab,
                            st_tab, pooled, out_rows, split, err);
     if (!has_next) break;

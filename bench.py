@@ -313,6 +313,20 @@ def summarize_profiles(out):
         lines.append(f"| {name} | {r['Calls']} | {r['TotalDurationNs']} | "
                      f"{float(r['AverageNs']):.0f} | {float(r['Percentage']):.2f} | "
                      f"{r['MinNs']} | {r['MaxNs']} |")
+    # per-launch durations of the GEMM from the trace: the first launches of a
+    # process run slower while clocks and translation caches settle, so the
+    # all-launch average above sits above the warm figure bench.py reports
+    trace = [r for r in csv.DictReader(open(_find_csv(os.path.join(out, "kt"), "kernel_trace.csv")))
+             if GEMM_KERNEL in r["Kernel_Name"]]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
+    if len(dur) > 15:
+        warm, last = dur[15:], dur[-10:]
+        lines += ["", f"`{GEMM_KERNEL}` per launch (ms, from the kernel trace, in launch order): "
+                  + ", ".join(f"{x:.3f}" for x in dur) + ".",
+                  f"Average after the 15 warm-up launches: {np.mean(warm):.3f} ms; average of "
+                  f"the last 10 (the per-kernel event pass that bench.py's roofline times): "
+                  f"{np.mean(last):.3f} ms."]
     lines += ["", f"Kernel source hash (gemm.hpp + pool.hpp + common.hpp): `{sha}`."]
     open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w").write("\n".join(lines) + "\n")
 

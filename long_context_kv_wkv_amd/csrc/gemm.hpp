@@ -83,9 +83,9 @@ __device__ __forceinline__ int gm_copy_row(int wave, int lane, int j) {
 // half of pair c+2, step 2c+1 the second), the second half the 2 panel
 // copies of step kt+3 (wave w copies column block w of the tile).  The copy
 // unit takes a 1 KiB copy every few tens of cycles and a wave cannot issue
-// past a copy it has not accepted, so the four waves of a SIMD pair place
-// their copies at different MFMAs (P = wave % 4).  Every group is fenced so
-// the compiler keeps this order.
+// past a copy it has not accepted, so waves on different SIMDs place their
+// copies at different MFMAs (P = wave % 4; other placements measured the
+// same).  Every group is fenced so the compiler keeps this order.
 // ---------------------------------------------------------------------------
 #define GM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | 0x0f70)
 // s_waitcnt vmcnt(6) lgkmcnt(0)

@@ -317,9 +317,13 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
   }
 }
 
-// The copy ring takes all of LDS; the epilogue's 1 KiB exchange sits in the
-// panel stage that is idle between two tiles (GM_IDLE_OFF).
+// The copy ring takes all of LDS; the epilogue's exchange (at most 3 KiB) sits
+// in the panel stage that is idle between two tiles (GM_IDLE_OFF).
 constexpr int POOL_LDS_BYTES = GM_LDS_BYTES;
+// ratio 4: [3 row-wave boundaries][2 column waves][32 lanes]; ratio 128:
+// [2 row-wave pairs][2 column waves][64 lanes]
+static_assert(3 * 2 * 32 * sizeof(Soft) <= GM_IDLE_BYTES && 2 * 2 * 64 * sizeof(Soft) <= GM_IDLE_BYTES,
+              "the epilogue exchange fits the idle panel stage");
 
 // One tile of a request: M-tile mt (its request b, the tile's first position
 // P0 and its index tloc among the request's tiles) and N-tile nt.

@@ -57,6 +57,7 @@ typedef enum {
 #define CMP_DEVERR_SEQLEN 4u     /* cu_seqlens not monotone / beyond T, seqused outside [0, slot], or
                                     more than 4 tokens in a decode request */
 #define CMP_DEVERR_OUT_ROWS 8u   /* sum over requests of ceil(n_b / ratio) > out_rows */
+#define CMP_DEVERR_SLOT 16u      /* compressor_epilog: slot_mapping[i] outside [-1, num_slots) */
 
 /*
  * Static shape of a Compressor layer.
@@ -201,6 +202,38 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* arg
  * errors are those of compressor_prefill. */
 int compressor_decode(const compressor_shape* shape, const compressor_args* args, void* stream);
 
+/* Quantised write of compressed rows into a paged FP8 cache, the step after
+ * the operator that stores its rows into the Lightning Indexer / Sparse Flash
+ * Attention compressed caches ([PyPTO] DeepSeek-V4 整网集成方式: those caches
+ * may be float8).  The page gives no more than that; this entry point takes
+ * the plainest reading:
+ *   format     OCP FP8 E4M3 (bias 7, largest finite 448, subnormals, no
+ *              infinity);
+ *   scaling    one fp32 scale per 128 consecutive channels of a row:
+ *              amax = max |x| of the block, scale = amax / 448, code =
+ *              E4M3 round-to-nearest-even of clamp(x * (448 / amax), +-448)
+ *              (fp32 arithmetic, correctly rounded); amax = 0 gives scale 0
+ *              and codes +-0;
+ *   placement  row i goes to cache row slot_mapping[i]; -1 writes nothing.
+ * rows          (device) bf16 [n_rows, head_dim], e.g. the out rows of
+ *               compressor_prefill / compressor_decode.
+ * n_rows        >= 0 (0: nothing is enqueued).
+ * head_dim      a multiple of 128, at most 8192 (CMP_ERR_INVALID otherwise).
+ * slot_mapping  (device) int32 [n_rows]: destination row of each row, or -1.
+ *               Destinations must be distinct.  A value outside
+ *               [-1, num_slots) writes nothing and sets CMP_DEVERR_SLOT.
+ * cache         (device) uint8 [num_slots, head_dim]: E4M3 codes, updated
+ *               in place (rows not named by slot_mapping keep their bytes).
+ * cache_scale   (device) fp32 [num_slots, head_dim / 128], likewise.
+ * num_slots     rows of cache (>= 0).
+ * device_error  (device) uint32 word the kernel ORs CMP_DEVERR_SLOT into (the
+ *               caller clears it); may be NULL.
+ * Returns CMP_OK, CMP_ERR_NULLPTR (a required pointer NULL with n_rows > 0),
+ * CMP_ERR_INVALID or CMP_ERR_HIP (launch failure). */
+int compressor_epilog(const void* rows, int32_t n_rows, int32_t head_dim,
+                      const int32_t* slot_mapping, void* cache, float* cache_scale,
+                      int64_t num_slots, uint32_t* device_error, void* stream);
+
 /* Synchronise `stream`, then read the device error word (CMP_DEVERR_* bits)
  * of the last call that used `workspace` into *code. */
 int compressor_last_device_error(const void* workspace, void* stream, int32_t* code);
@@ -213,7 +246,7 @@ const char* compressor_status_str(int status);
  * records.  Kernel names: "plan", "hadamard_pack", "prefix", "gemm" (projection
  * with the window pooling and state stores in its epilogue), "post",
  * "decode_main" (GEMV and ring pre-pooling),
- * "decode_tail", "pack", "state_fill". */
+ * "decode_tail", "pack", "state_fill", "epilog". */
 int compressor_timing_enable(int32_t on);
 
 /* Wait for the recorded events, then report the number of launches of

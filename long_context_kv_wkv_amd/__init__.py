@@ -20,13 +20,13 @@ LIB_PATH = os.path.join(_HERE, "libcompressor.so")
 CMP_OK = 0
 STATUS = {0: "CMP_OK", 1: "CMP_ERR_NULLPTR", 2: "CMP_ERR_INVALID", 3: "CMP_ERR_UNSUPPORTED",
           4: "CMP_ERR_WORKSPACE", 5: "CMP_ERR_OUT_ROWS", 6: "CMP_ERR_HIP"}
-DEVERR_TABLE, DEVERR_START_POS, DEVERR_SEQLEN, DEVERR_OUT_ROWS = 1, 2, 4, 8
+DEVERR_TABLE, DEVERR_START_POS, DEVERR_SEQLEN, DEVERR_OUT_ROWS, DEVERR_SLOT = 1, 2, 4, 8, 16
 
 EXPORTS = ("compressor_prefill_workspace_size", "compressor_decode_workspace_size",
            "compressor_pack_weights", "compressor_state_init", "compressor_state_reset",
            "compressor_prefill", "compressor_decode", "compressor_last_device_error",
            "compressor_status_str", "compressor_timing_enable", "compressor_timing_query",
-           "nsa_compress_with_cache")
+           "compressor_epilog", "nsa_compress_with_cache")
 NSA_BF16, NSA_F16 = 0, 1
 NSA_LAYOUT_PAGED, NSA_LAYOUT_TND = 0, 1
 NSA_DEVERR_SLOT, NSA_DEVERR_TABLE, NSA_DEVERR_SEQLEN = 1, 2, 4
@@ -101,6 +101,7 @@ def library():
             "compressor_timing_enable": (i32,),
             "compressor_timing_query": (ctypes.c_char_p, ctypes.POINTER(i32),
                                         ctypes.POINTER(ctypes.c_double)),
+            "compressor_epilog": (vp, i32, i32, vp, vp, vp, ctypes.c_int64, vp, vp),
             "nsa_compress_with_cache": (ctypes.POINTER(NsaShape), ctypes.POINTER(NsaArgs), vp),
         }
         for name, argt in sig.items():
@@ -238,6 +239,24 @@ def compressor_timing_query(kernel: str):
     _check("compressor_timing_query", library().compressor_timing_query(
         kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+def compressor_epilog(rows: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tensor,
+                      cache_scale: torch.Tensor, device_error: torch.Tensor = None,
+                      stream=None) -> None:
+    """rows bf16 [n, D]; slot_mapping int32 [n] (-1: no slot); cache uint8
+    [num_slots, D] (E4M3 codes) and cache_scale fp32 [num_slots, D / 128],
+    both updated in place; device_error an int32 [1] word the kernel ORs
+    DEVERR_SLOT into."""
+    n, d = rows.shape
+    if slot_mapping.numel() != n or cache.dim() != 2 or cache.shape[1] != d:
+        raise ValueError("compressor_epilog: shapes of rows, slot_mapping and cache disagree")
+    if cache_scale.shape != (cache.shape[0], d // 128):
+        raise ValueError("compressor_epilog: cache_scale must be [num_slots, D / 128]")
+    _check("compressor_epilog", library().compressor_epilog(
+        _dev(rows, torch.bfloat16, "rows"), n, d, _dev(slot_mapping, torch.int32, "slot_mapping"),
+        _dev(cache, torch.uint8, "cache"), _dev(cache_scale, torch.float32, "cache_scale"),
+        int(cache.shape[0]), _dev(device_error, torch.int32, "device_error"), _stream(stream)))
 
 
 # --------------------------------------------------------------------------

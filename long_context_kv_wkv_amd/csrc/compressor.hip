@@ -17,6 +17,7 @@
 #include "pool.hpp"
 #include "prefill.hpp"
 #include "nsa.hpp"
+#include "epilog.hpp"
 
 using namespace cmp;
 
@@ -502,6 +503,26 @@ int compressor_timing_query(const char* kernel, int32_t* launches, double* total
   return CMP_OK;
 }
 
+
+int compressor_epilog(const void* rows, int32_t n_rows, int32_t head_dim,
+                      const int32_t* slot_mapping, void* cache, float* cache_scale,
+                      int64_t num_slots, uint32_t* device_error, void* stream) {
+  if (n_rows < 0 || num_slots < 0 || head_dim <= 0 || head_dim % EPL_BLOCK || head_dim > 8192)
+    return CMP_ERR_INVALID;
+  const int nblk_row = head_dim / EPL_BLOCK;
+  const long n_blocks = (long)n_rows * nblk_row;
+  if (n_blocks > 0x7fffffffL - EPL_THREADS * EPL_GROUP_BLOCKS) return CMP_ERR_INVALID;
+  if (n_rows == 0) return CMP_OK;
+  if (!rows || !slot_mapping || !cache || !cache_scale) return CMP_ERR_NULLPTR;
+  const long groups = (n_blocks + EPL_GROUP_BLOCKS - 1) / EPL_GROUP_BLOCKS;
+  const long grid = (groups + EPL_THREADS / 16 - 1) / (EPL_THREADS / 16);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch("epilog", s, [&] {
+    hipLaunchKernelGGL(epilog_kernel, dim3((unsigned)grid), dim3(EPL_THREADS), 0, s,
+                       static_cast<const uint16_t*>(rows), (int)n_blocks, nblk_row, slot_mapping,
+                       static_cast<uint8_t*>(cache), cache_scale, (long)num_slots, device_error);
+  });
+}
 
 int nsa_compress_with_cache(const nsa_shape* sh, const nsa_args* a, void* stream) {
   if (!sh || !a) return CMP_ERR_NULLPTR;

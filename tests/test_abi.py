@@ -104,3 +104,14 @@ def test_nsa_shape_checks_before_any_launch():
                 cmp.make_nsa_shape(32, 128, 32, 16, 128, 2, 0),    # dtype
                 cmp.make_nsa_shape(32, 128, 32, 16, 128, 0, 2)):   # layout
         assert lib.nsa_compress_with_cache(ctypes.byref(bad), ctypes.byref(args), None) == 3
+
+
+def test_epilog_argument_checks_before_any_launch():
+    lib = cmp.library()
+    f = lib.compressor_epilog
+    assert f(None, 0, 512, None, None, None, 0, None, None) == 0          # nothing to do
+    assert f(None, 4, 512, None, None, None, 8, None, None) == 1          # NULL rows
+    for n, d, slots in ((4, 100, 8), (4, 0, 8), (4, 8320, 8), (-1, 512, 8), (4, 512, -1)):
+        assert f(None, n, d, None, None, None, slots, None, None) == 2, (n, d, slots)
+    # the block count must stay below 2^31
+    assert f(None, 2 ** 31 - 1, 8192, None, None, None, 8, None, None) == 2

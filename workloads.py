@@ -335,3 +335,46 @@ def build_nsa(spec: NsaSpec, seed: int) -> dict:
 # 16, 32 heads of 128), paged with 128-token pages
 NSA_DECODE = NsaSpec("nsa_decode", head_num=32, head_dim=128, cbs=32, stride=16, page=128,
                      dtype="bf16", layout="paged", batch=128, max_len=256, fire_fraction=1.0)
+
+
+# --------------------------------------------------------------------------
+# Quantised cache write after the operator (compressor_epilog): compressed
+# rows bf16 [rows, D] with blocks of 128 channels at mixed magnitudes (as
+# normalised rows times weights of various sizes), a slot mapping that is a
+# seeded permutation into a larger cache with every `skip`-th row at -1, and
+# a cache pre-filled with random bytes and scales (rows nobody writes must
+# keep them).
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class EpilogSpec:
+    name: str
+    rows: int
+    head_dim: int
+    num_slots: int
+    skip: int = 0                 # every skip-th row has slot -1 (0: none)
+    bad_slots: tuple = ()         # (row, slot) pairs set after the permutation
+
+
+def build_epilog(spec: EpilogSpec, seed: int) -> dict:
+    rng = np.random.default_rng(seed)
+    nb = spec.head_dim // 128
+    x = rng.standard_normal((spec.rows, spec.head_dim)).astype(np.float32)
+    mag = rng.choice(np.float32([1e-3, 0.05, 1.0, 30.0]), (spec.rows, nb))
+    x *= np.repeat(mag, 128, axis=1)
+    slots = rng.permutation(spec.num_slots)[: spec.rows].astype(np.int32)
+    if spec.skip:
+        slots[:: spec.skip] = -1
+    for r, s in spec.bad_slots:
+        slots[r] = s
+    return {"rows": f32_to_bf16_bits(x), "slot_mapping": slots,
+            "cache": rng.integers(0, 256, (spec.num_slots, spec.head_dim), dtype=np.uint8),
+            "cache_scale": rng.standard_normal((spec.num_slots, nb)).astype(np.float32),
+            "head_dim": spec.head_dim}
+
+
+# the 128K C4A output (32768 rows of D = 512), the indexer's D = 128 rows
+# and a ragged case with rows that name no slot or a slot outside the cache
+EPILOG_C4A = EpilogSpec("epilog_c4a_128k", rows=32768, head_dim=512, num_slots=40000, skip=7)
+EPILOG_INDEXER = EpilogSpec("epilog_indexer", rows=64, head_dim=128, num_slots=64)
+EPILOG_RAGGED = EpilogSpec("epilog_ragged", rows=37, head_dim=128, num_slots=50, skip=5,
+                           bad_slots=((3, -2), (11, 50)))

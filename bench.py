@@ -176,6 +176,57 @@ def bench_decode(name, steps, warmup, copies=12):
                 panel_bytes=panel_bytes, step_bytes=decode_bytes(w))
 
 
+def bench_epilog(steps, copies=9):
+    """One compressor_epilog call on the 128K C4A output shape (32768 rows of
+    D = 512 into a 40000-row FP8 cache, every 7th row without a slot) in
+    device time: calls over `copies` sets of rows and caches (> the 256 MB
+    last-level cache) captured in a HIP graph and replayed."""
+    import torch
+    import long_context_kv_wkv_amd as cmp
+    import workloads
+
+    w = workloads.build_epilog(workloads.EPILOG_C4A, workloads.SEED_BASE + 710)
+    dev = "cuda:0"
+    rows = torch.from_numpy(w["rows"].view(np.int16)).to(dev).view(torch.bfloat16)
+    slots = torch.from_numpy(w["slot_mapping"]).to(dev)
+    sets = [(rows.clone(), torch.from_numpy(w["cache"]).to(dev),
+             torch.from_numpy(w["cache_scale"]).to(dev)) for _ in range(copies)]
+
+    def run(j):
+        r, c, sc = sets[j % copies]
+        cmp.compressor_epilog(r, slots, c, sc)
+
+    for j in range(3):
+        run(j)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for j in range(copies):
+            run(j)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // copies)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1000.0 / (reps * copies)
+    n, d = w["rows"].shape
+    written = int(np.sum(w["slot_mapping"] >= 0))
+    nbytes = n * d * 2 + n * 4 + written * (d + 4 * (d // 128))
+    return {"us_per_call": us, "rows": n, "rows_written": written, "algorithmic_bytes": nbytes,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "config": "32768 rows x 512 bf16 -> FP8 E4M3 cache rows + fp32 scale per 128"}
+
+
 def bench_nsa(steps, copies=9):
     """One NsaCompressWithCache call (128 sequences that all compress) in
     device time: calls over `copies` caches (> the 256 MB last-level cache in
@@ -400,6 +451,7 @@ def main():
     if a.decode_only:
         for name in DECODE_WORKLOADS:
             print(name, json.dumps(bench_decode(name, a.decode_steps, 5)), flush=True)
+        print("epilog_fp8", json.dumps(bench_epilog(a.decode_steps)), flush=True)
         return
     pre = bench_prefill(a.steps, a.warmup)
     w = pre["w"]
@@ -440,6 +492,7 @@ def main():
                          / PEAK_HBM_GBS}
         result["decode"] = dec
         result["nsa_compress"] = bench_nsa(a.decode_steps)
+        result["epilog_fp8"] = bench_epilog(a.decode_steps)
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)

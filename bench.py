@@ -49,13 +49,13 @@ def load_traffic(profile_name, sha):
     return d.get("hbm_bytes_per_launch")
 
 
-def bench_prefill(steps, warmup):
+def bench_prefill(steps, warmup, name="c4a_128k"):
     import torch
     import gpu_harness
     import long_context_kv_wkv_amd as cmp
     import workloads
 
-    w = workloads.build_named("c4a_128k")
+    w = workloads.build_named(name)
     case = gpu_harness.DeviceCase(w)
     for _ in range(warmup):
         case.prefill()
@@ -493,6 +493,18 @@ def main():
         result["decode"] = dec
         result["nsa_compress"] = bench_nsa(a.decode_steps)
         result["epilog_fp8"] = bench_epilog(a.decode_steps)
+        # the other prefill workloads: the 8192-token C128A call and the
+        # packed variable-length C4A continuation (8 requests, 88826 tokens)
+        other = {}
+        for name in ("c128a_8192", "varlen_c4a"):
+            p = bench_prefill(10, 5, name)
+            pw = p["w"]
+            fl = 2.0 * pw["T"] * pw["hidden"] * 2 * pw["coff"] * pw["head_dim"]
+            other[name] = {"ms_per_step": p["ms_per_step"], "kernels_ms": p["kernels"],
+                           "gemm_tflops": fl / (p["kernels"]["gemm"] * 1e-3) / 1e12,
+                           "gemm_mfma_frac": fl / (p["kernels"]["gemm"] * 1e-3) / 1e12
+                           / PEAK_BF16_TFLOPS, "tokens": pw["T"]}
+        result["prefill_other"] = other
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)

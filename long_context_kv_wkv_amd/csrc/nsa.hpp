@@ -43,7 +43,7 @@ template <int CBS>
 __global__ __launch_bounds__(NSA_THREADS) void nsa_compress_kernel(
     NsaCfg cf, const uint16_t* __restrict__ in, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ slot_mapping, const int64_t* __restrict__ act,
-    const int32_t* __restrict__ table, int B, int table_stride, int num_blocks, long T,
+    const int32_t* __restrict__ table, int /*batch: the grid's x*/, int table_stride, int num_blocks, long T,
     uint16_t* __restrict__ out, long result_len, uint32_t* __restrict__ err) {
   __shared__ long s_cu;
   __shared__ int32_t s_tab[NSA_THREADS];

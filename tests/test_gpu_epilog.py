@@ -118,3 +118,39 @@ def test_epilog_of_prefill_output(lib):
     cscale = np.zeros((n, d // 128), np.float32)
     got = _run(lib, out, slots, cache, cscale)
     _check(out, slots, cache, cscale, got)
+
+
+def test_epilog_graph_replay_matches_eager(lib):
+    """A captured call (one kernel, no memset, no allocation) replays to the
+    eager result; every replay is checked, with eager work and a
+    synchronisation between replays."""
+    _announce("epilog graph replay")
+    w = W.build_epilog(W.EPILOG_INDEXER, W.SEED_BASE + 711)
+    dev = "cuda:0"
+    rows = torch.from_numpy(w["rows"].view(np.int16)).to(dev).view(torch.bfloat16)
+    slots = torch.from_numpy(w["slot_mapping"]).to(dev)
+    cache0 = torch.from_numpy(w["cache"]).to(dev)
+    scale0 = torch.from_numpy(w["cache_scale"]).to(dev)
+    cache, scale = cache0.clone(), scale0.clone()
+    lib.compressor_epilog(rows, slots, cache, scale)
+    torch.cuda.synchronize()
+    want_c, want_s = cache.cpu().numpy(), scale.cpu().numpy()
+    gc, gs = cache0.clone(), scale0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lib.compressor_epilog(rows, slots, gc, gs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lib.compressor_epilog(rows, slots, gc, gs)
+    for rep in range(3):
+        gc.copy_(cache0)
+        gs.copy_(scale0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gc.cpu().numpy(), want_c), rep
+        assert np.array_equal(gs.cpu().numpy().view(np.uint32), want_s.view(np.uint32)), rep
+        lib.compressor_epilog(rows, slots, cache, scale)        # eager work in between

@@ -241,6 +241,17 @@ int compressor_last_device_error(const void* workspace, void* stream, int32_t* c
 /* Static text of a status code. */
 const char* compressor_status_str(int status);
 
+/* Row height of the prefill projection tiles for every later
+ * compressor_prefill call of the process.  0 (the default): 256-row tiles
+ * (8 waves per workgroup), or 128-row tiles (4 waves) when the call is too
+ * short for ceil(T / 256) x (column tiles) to reach the device's compute unit
+ * count, so that every unit gets work.  128 or 256 forces that height (for
+ * measurement and tests; results agree within rounding, not bit for bit,
+ * since the height decides which rows a tile's epilogue pools together).
+ * Returns CMP_OK, or CMP_ERR_INVALID for any other value (setting unchanged).
+ * Not ordered with calls already running on other threads. */
+int compressor_set_prefill_tile_rows(int32_t rows);
+
 /* Kernel timing: while enabled, every kernel the library enqueues is
  * bracketed by a pair of HIP events on the same stream.  Enabling clears the
  * records.  Kernel names: "plan", "hadamard_pack", "prefix", "gemm" (projection

@@ -26,7 +26,7 @@ EXPORTS = ("compressor_prefill_workspace_size", "compressor_decode_workspace_siz
            "compressor_pack_weights", "compressor_state_init", "compressor_state_reset",
            "compressor_prefill", "compressor_decode", "compressor_last_device_error",
            "compressor_status_str", "compressor_timing_enable", "compressor_timing_query",
-           "compressor_epilog", "nsa_compress_with_cache")
+           "compressor_epilog", "compressor_set_prefill_tile_rows", "nsa_compress_with_cache")
 NSA_BF16, NSA_F16 = 0, 1
 NSA_LAYOUT_PAGED, NSA_LAYOUT_TND = 0, 1
 NSA_DEVERR_SLOT, NSA_DEVERR_TABLE, NSA_DEVERR_SEQLEN = 1, 2, 4
@@ -99,6 +99,7 @@ def library():
             "compressor_decode": (sp, ap, vp),
             "compressor_last_device_error": (vp, vp, ctypes.POINTER(i32)),
             "compressor_timing_enable": (i32,),
+            "compressor_set_prefill_tile_rows": (i32,),
             "compressor_timing_query": (ctypes.c_char_p, ctypes.POINTER(i32),
                                         ctypes.POINTER(ctypes.c_double)),
             "compressor_epilog": (vp, i32, i32, vp, vp, vp, ctypes.c_int64, vp, vp),
@@ -226,6 +227,12 @@ def compressor_last_device_error(workspace: torch.Tensor, stream=None) -> int:
 
 def compressor_status_str(status: int) -> str:
     return library().compressor_status_str(status).decode()
+
+
+def compressor_set_prefill_tile_rows(rows: int) -> None:
+    """Prefill projection tile height for later calls: 0 = automatic (256,
+    or 128 for calls too short to fill the device), 128 or 256 = forced."""
+    _check("compressor_set_prefill_tile_rows", library().compressor_set_prefill_tile_rows(int(rows)))
 
 
 def compressor_timing_enable(on: bool) -> None:

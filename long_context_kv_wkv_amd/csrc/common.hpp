@@ -82,6 +82,7 @@ enum PlanField {
 // Static configuration passed by value to kernels.
 struct Cfg {
   int ratio, coff, D, H, N, rope, rotate, bs, nblocks, stride;
+  int bm;   // prefill GEMM tile rows (256, or 128 for short calls)
 };
 
 // Ring slot of position p, and its (block, row) through a table row.

@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -88,6 +89,7 @@ int check_shape(const compressor_shape* sh, Cfg* cf) {
     return CMP_ERR_INVALID;
   cf->ratio = sh->ratio;
   cf->coff = coff;
+  cf->bm = 256;
   cf->D = sh->head_dim;
   cf->H = sh->hidden;
   cf->N = 2 * coff * sh->head_dim;
@@ -102,9 +104,9 @@ int check_shape(const compressor_shape* sh, Cfg* cf) {
 // The kernel of each ratio (coff = 2 only at ratio 4).
 template <int R>
 constexpr int coff_of() { return R == 4 ? 2 : 1; }
-template <int R>
+template <int R, int WV>
 const void* gemm_kernel_of() {
-  return reinterpret_cast<const void*>(gemm_pool_kernel<R, coff_of<R>()>);
+  return reinterpret_cast<const void*>(gemm_pool_kernel<R, coff_of<R>(), WV>);
 }
 // Calls f.template operator()<R>() for the compile-time ratio equal to r.
 template <typename F>
@@ -119,6 +121,9 @@ void with_ratio(int r, F&& f) {
     default: f.template operator()<128>(); break;
   }
 }
+
+// Prefill tile height set by compressor_set_prefill_tile_rows (0: automatic).
+std::atomic<int> g_tile_rows{0};
 
 // Compute units of the current device (cached per device).
 int device_cu_count() {
@@ -142,7 +147,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct PrefillLayout {
   size_t err, tiles, hadflag, plan, pooled, hadF, staging, split, total;
 };
-int prefill_max_tiles(const Cfg& cf, int T, int B);
+int prefill_max_tiles(int T, int B, int bm);
 PrefillLayout prefill_layout(const Cfg& cf, int T, int B, int out_rows) {
   PrefillLayout L;
   size_t o = 0;
@@ -153,16 +158,16 @@ PrefillLayout prefill_layout(const Cfg& cf, int T, int B, int out_rows) {
   L.pooled = o;   o = align256(o + (size_t)out_rows * cf.D * 4);
   L.hadF = o;     o = align256(o + (cf.rotate ? (size_t)cf.D * cf.D * 2 : 0));
   L.staging = o;  o = align256(o + (size_t)B * cf.coff * cf.ratio * 2 * cf.coff * cf.D * 4);
-  L.split = o;    o = align256(o + (cf.coff == 2 ? (size_t)prefill_max_tiles(cf, T, B) * 6 * cf.D * 4 : 0));
+  // sized for the shorter tiles, whichever the call runs
+  L.split = o;    o = align256(o + (cf.coff == 2 ? (size_t)prefill_max_tiles(T, B, 128) * 6 * cf.D * 4 : 0));
   L.total = o;
   return L;
 }
 
-// Upper bound of the M-tiles of a call (each request adds at most two to
-// its share of T / step).
-int prefill_max_tiles(const Cfg& cf, int T, int B) {
-  (void)cf;
-  return (T + GM_BM - 1) / GM_BM + 2 * B;
+// Upper bound of the M-tiles of a call with bm-row tiles (each request adds
+// at most two to its share of T / bm).
+int prefill_max_tiles(int T, int B, int bm) {
+  return (T + bm - 1) / bm + 2 * B;
 }
 
 // decode split: K ranges per 32-column block so that about 256+ workgroups
@@ -228,10 +233,13 @@ int ensure_lds_limits() {
     hipError_t e1 = hipSuccess;
     for (int r = 2; r <= 128; r *= 2)
       with_ratio(r, [&]<int R>() {
-        const hipError_t e = hipFuncSetAttribute(gemm_kernel_of<R>(),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 POOL_LDS_BYTES);
-        if (e1 == hipSuccess) e1 = e;
+        const hipError_t e8 = hipFuncSetAttribute(gemm_kernel_of<R, 8>(),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  Gm<8>::LDS_BYTES);
+        const hipError_t e4 = hipFuncSetAttribute(gemm_kernel_of<R, 4>(),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  Gm<4>::LDS_BYTES);
+        if (e1 == hipSuccess) e1 = e8 != hipSuccess ? e8 : e4;
       });
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(post_kernel<8>),
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -247,6 +255,12 @@ int ensure_lds_limits() {
 }  // namespace
 
 extern "C" {
+
+int compressor_set_prefill_tile_rows(int32_t rows) {
+  if (rows != 0 && rows != 128 && rows != 256) return CMP_ERR_INVALID;
+  g_tile_rows.store(rows, std::memory_order_relaxed);
+  return CMP_OK;
+}
 
 const char* compressor_status_str(int status) {
   switch (status) {
@@ -346,10 +360,16 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
   float* split = reinterpret_cast<float*>(ws + L.split);
   const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
   const int B = a->batch, T = a->T;
+  // GEMM tile height: 256 rows (8 waves), or 128 (4 waves) when the call is
+  // too short to give every CU a 256-row tile
+  const int tiles_n = cf.N / GM_BN;
+  const int cus = device_cu_count() / 8 * 8;
+  const int forced = g_tile_rows.load(std::memory_order_relaxed);
+  cf.bm = forced ? forced : (long)((T + 255) / 256) * tiles_n < cus ? 128 : 256;
 
   CMP_TRY(launch("plan", st, [&] {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, a->cu_seqlens,
-                       a->seqused, a->start_pos, B, T, cf.ratio, cf.coff, GM_BM, a->out_rows,
+                       a->seqused, a->start_pos, B, T, cf.ratio, cf.coff, cf.bm, a->out_rows,
                        plan, tiles, err, had_general);
   }));
   if (cf.rotate) {
@@ -366,13 +386,17 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
     }));
     // persistent: one workgroup per CU (a multiple of 8, one run of tiles
     // per XCD), never more than there are tiles
-    const int tiles_n = cf.N / GM_BN;
-    const long nwg = (long)prefill_max_tiles(cf, T, B) * tiles_n;
-    const int grid = int(std::min<long>(device_cu_count() / 8 * 8, (nwg + 7) / 8 * 8));
+    const long nwg = (long)prefill_max_tiles(T, B, cf.bm) * tiles_n;
+    const int grid = int(std::min<long>(cus, (nwg + 7) / 8 * 8));
     CMP_TRY(launch("gemm", st, [&] {
-      decltype(&gemm_pool_kernel<4, 2>) kern = nullptr;
-      with_ratio(cf.ratio, [&]<int R>() { kern = gemm_pool_kernel<R, coff_of<R>()>; });
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(GM_THREADS), POOL_LDS_BYTES, st, cf,
+      decltype(&gemm_pool_kernel<4, 2, 8>) kern = nullptr;
+      with_ratio(cf.ratio, [&]<int R>() {
+        kern = cf.bm == 128 ? gemm_pool_kernel<R, coff_of<R>(), 4>
+                            : gemm_pool_kernel<R, coff_of<R>(), 8>;
+      });
+      const int threads = cf.bm == 128 ? Gm<4>::THREADS : Gm<8>::THREADS;
+      const int lds = cf.bm == 128 ? Gm<4>::LDS_BYTES : Gm<8>::LDS_BYTES;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, cf,
                          static_cast<const uint16_t*>(a->x),
                          static_cast<const uint16_t*>(a->w_packed), T, B, plan, tiles, a->ape,
                          staging, a->kv_state, a->score_state, kvt, a->state_block_table, pooled,

@@ -12,7 +12,9 @@
 // faster at the 128K C4A shape, although every wave now reads half of a
 // fragment set it shares with three others).  K step 32, operands staged in
 // LDS by direct-to-LDS copies (global_load_lds_dwordx4: no staging
-// registers, no ds_write), all 160 KiB of the CU's LDS:
+// registers, no ds_write), all 160 KiB of the CU's LDS.  Calls too short to
+// give every CU a 256-row tile run 4 waves (2 x 2) on 128 x 256 tiles
+// instead (same wave sub-tile, 112 KiB of LDS), so that the chip fills:
 //  * X: three 32 KiB buffers, each two K steps (256 rows x 128 B), so every
 //    copy fetches whole 128-byte cache lines (8 rows x 128 B per copy
 //    instruction).  Rows are row-major with their 16-byte chunks
@@ -41,16 +43,26 @@
 
 namespace cmp {
 
-constexpr int GM_BM = 256, GM_BN = 256, GM_BK = 32;
-constexpr int GM_WAVES = 8;
-constexpr int GM_THREADS = 64 * GM_WAVES;
+constexpr int GM_BN = 256, GM_BK = 32;
 constexpr int GM_WROWS = 64;                                   // rows of a wave's sub-tile
 constexpr int GM_W_STAGE_BYTES = GM_BN * GM_BK * 2;            // 16 KiB
-constexpr int GM_X_BUF_BYTES = GM_BM * 2 * GM_BK * 2;          // 32 KiB: two K steps
 constexpr int GM_X_OFF = 4 * GM_W_STAGE_BYTES;                 // panel stages first
-constexpr int GM_LDS_BYTES = GM_X_OFF + 3 * GM_X_BUF_BYTES;    // 160 KiB
-constexpr int GM_A_COPIES = GM_X_BUF_BYTES / 1024 / GM_WAVES;  // X copies per wave and buffer (4)
+constexpr int GM_A_COPIES = 4;                                 // X copies per wave and buffer
 constexpr int GM_A_ROWS = 1024 / (2 * GM_BK * 2);              // X rows per copy instruction (8)
+
+// The two tile shapes, by wave count WV: 8 waves (4 row-waves x 2) make a
+// 256 x 256 tile; 4 waves (2 x 2) a 128 x 256 tile.  The wave sub-tile
+// (64 x 128) and the per-wave X copies are the same.
+template <int WV>
+struct Gm {
+  static constexpr int THREADS = 64 * WV;
+  static constexpr int BM = 32 * WV;                           // tile rows
+  static constexpr int NWM = BM / GM_WROWS;                    // row-waves
+  static constexpr int X_BUF_BYTES = BM * 2 * GM_BK * 2;       // BM rows x two K steps
+  static constexpr int LDS_BYTES = GM_X_OFF + 3 * X_BUF_BYTES; // 160 / 112 KiB
+  static constexpr int WC = 16 / WV;                           // panel copies per wave and step
+  static_assert(X_BUF_BYTES / 1024 / WV == GM_A_COPIES, "X copies per wave");
+};
 // LDS the epilogue may use between two tiles: the panel stage of a tile's
 // last K step, which nothing reads or fills until the next tile's first step.
 constexpr int GM_IDLE_OFF = 3 * GM_W_STAGE_BYTES;
@@ -88,8 +100,8 @@ __device__ __forceinline__ int gm_copy_row(int wave, int lane, int j) {
 // same).  Every group is fenced so the compiler keeps this order.
 // ---------------------------------------------------------------------------
 #define GM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | 0x0f70)
-// s_waitcnt vmcnt(6) lgkmcnt(0)
-#define GM_WAIT_VM6_LGKM0() __builtin_amdgcn_s_waitcnt(6 | 0x0070)
+// s_waitcnt vmcnt(n) lgkmcnt(0)
+#define GM_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | 0x0070)
 #define GM_BARRIER() asm volatile("s_barrier" ::: "memory")
 
 // Copy sources of one tile: a uniform base for X (the tile's first row) and
@@ -105,7 +117,8 @@ struct GmSrc {
 // arow[j] is the X row that this lane's j-th copy instruction reads (tile row
 // gm_copy_row(wave, lane, j)); rows outside the tensor must be clamped by the
 // caller to any valid row (their results are not used).  arow0 (uniform)
-// <= every arow[j] and arow[j] - arow0 < GM_BM.
+// <= every arow[j] and arow[j] - arow0 < the tile rows.
+template <int WV>
 __device__ __forceinline__ GmSrc gm_sources(const uint16_t* __restrict__ X,
                                             const uint16_t* __restrict__ W, int K, int n0,
                                             const int (&arow)[GM_A_COPIES], int arow0) {
@@ -121,19 +134,22 @@ __device__ __forceinline__ GmSrc gm_sources(const uint16_t* __restrict__ X,
     src.a[j] = (uint32_t)(((size_t)(arow[j] - arow0) * K + kc * 8) * 2);
   }
   src.x = reinterpret_cast<const uint8_t*>(X + (size_t)__builtin_amdgcn_readfirstlane(arow0) * K);
-  // panel copies: wave w copies column block w (fragments (w, k-step) of a
-  // stage); lane offsets come from gm_woff
+  // panel copies: wave w copies column blocks w*WC/2 .. (fragments (block,
+  // k-step) of a stage); lane offsets come from gm_woff
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  src.w = reinterpret_cast<const uint8_t*>(W + (((size_t)(n0 >> 5) + wv) * (size_t)(K >> 4)) * 512);
+  src.w = reinterpret_cast<const uint8_t*>(
+      W + (((size_t)(n0 >> 5) + wv * (Gm<WV>::WC / 2)) * (size_t)(K >> 4)) * 512);
   return src;
 }
 
+template <int WV>
 __device__ __forceinline__ uint8_t* gm_xbuf(uint8_t* smem, int buf) {
-  return smem + GM_X_OFF + buf * GM_X_BUF_BYTES;
+  return smem + GM_X_OFF + buf * Gm<WV>::X_BUF_BYTES;
 }
-// Byte offset of k-step g of K step t in a column block of the panel.
-__device__ __forceinline__ uint32_t gm_woff(int g, int t) {
-  return (uint32_t)(((t * 2 + g) << 10) + (threadIdx.x & 63) * 16);
+// Byte offset of this wave's panel copy c of K step t (column block c / 2
+// of the wave's, k-step c % 2; a column block is ksteps fragments of 1 KiB).
+__device__ __forceinline__ uint32_t gm_woff(int c, int t, int ksteps) {
+  return (uint32_t)((((c >> 1) * ksteps + t * 2 + (c & 1)) << 10) + (threadIdx.x & 63) * 16);
 }
 // Quarter q of the X copies of K-step pair c into buffer xb.
 __device__ __forceinline__ void gm_xcopy(const GmSrc& src, int c, int q, uint8_t* xb) {
@@ -144,24 +160,27 @@ __device__ __forceinline__ void gm_xcopy(const GmSrc& src, int c, int q, uint8_t
           xb + (wave * GM_A_COPIES + 2 * q + g) * 1024);
 }
 // The panel copies of K step t into stage st.
-__device__ __forceinline__ void gm_wcopy(const GmSrc& src, int t, uint8_t* st) {
+template <int WV>
+__device__ __forceinline__ void gm_wcopy(const GmSrc& src, int t, uint8_t* st, int ksteps) {
+  constexpr int WC = Gm<WV>::WC;
   const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int g = 0; g < 2; ++g) dma16(src.w + gm_woff(g, t), st + (wave * 2 + g) * 1024);
+  for (int c = 0; c < WC; ++c) dma16(src.w + gm_woff(c, t, ksteps), st + (wave * WC + c) * 1024);
 }
 
 // The copies of steps 0 .. 2 of a workgroup's first tile (pairs 0 and 1 into
 // X buffers 0 and 1, steps 0 .. 2 into panel stages 0 .. 2), in the order the
 // steady state issues them; later tiles get theirs from the previous tile's
 // last steps.
-__device__ __forceinline__ void gm_prologue(uint8_t* smem, const GmSrc& src) {
-  gm_xcopy(src, 0, 0, gm_xbuf(smem, 0));
-  gm_xcopy(src, 0, 1, gm_xbuf(smem, 0));
-  gm_wcopy(src, 0, smem);
-  gm_xcopy(src, 1, 0, gm_xbuf(smem, 1));
-  gm_wcopy(src, 1, smem + GM_W_STAGE_BYTES);
-  gm_xcopy(src, 1, 1, gm_xbuf(smem, 1));
-  gm_wcopy(src, 2, smem + 2 * GM_W_STAGE_BYTES);
+template <int WV>
+__device__ __forceinline__ void gm_prologue(uint8_t* smem, const GmSrc& src, int ksteps) {
+  gm_xcopy(src, 0, 0, gm_xbuf<WV>(smem, 0));
+  gm_xcopy(src, 0, 1, gm_xbuf<WV>(smem, 0));
+  gm_wcopy<WV>(src, 0, smem, ksteps);
+  gm_xcopy(src, 1, 0, gm_xbuf<WV>(smem, 1));
+  gm_wcopy<WV>(src, 1, smem + GM_W_STAGE_BYTES, ksteps);
+  gm_xcopy(src, 1, 1, gm_xbuf<WV>(smem, 1));
+  gm_wcopy<WV>(src, 2, smem + 2 * GM_W_STAGE_BYTES, ksteps);
 }
 
 // The K loop of one tile; xrot = X buffer of its K-step pair 0.  Step kt
@@ -171,9 +190,14 @@ __device__ __forceinline__ void gm_prologue(uint8_t* smem, const GmSrc& src) {
 // first stages are in flight while this tile's epilogue runs.  KT % 4 == 0
 // keeps the panel stage of step kt at kt % 4 in every tile; the X buffers
 // continue their rotation into the next tile.
-template <int P>
+template <int WV, int P>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[2][4], uint8_t* smem, const GmSrc& cur,
-                                          const GmSrc& nxt, bool has_next, int KT, int xrot) {
+                                          const GmSrc& nxt, bool has_next, int KT, int xrot,
+                                          int ksteps) {
+  constexpr int WC = Gm<WV>::WC;
+  // outstanding copies allowed at the mid-step wait (step kt-1's and the
+  // first half of step kt's) and at the tile start (pair 1's, steps 1 and 2)
+  constexpr int VM_MID = 2 + WC + 2, VM_START = 4 + 2 * WC;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int lrow = lane & 31, lhalf = lane >> 5;
@@ -184,10 +208,10 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[2][4], uint8_t* smem, co
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // step 0's stage and pair 0 have landed once at most the 8 newest memory
-  // operations are outstanding (copies of pair 1 and steps 1 and 2, or the
-  // previous epilogue's stores, which come after them)
-  GM_WAIT_VM(8);
+  // step 0's stage and pair 0 have landed once at most the VM_START newest
+  // memory operations are outstanding (copies of pair 1 and steps 1 and 2,
+  // or the previous epilogue's stores, which come after them)
+  GM_WAIT_VM(VM_START);
   GM_BARRIER();
   // X buffers of pairs kc, kc + 1, kc + 2
   int xb0 = xrot, xb1 = xrot == 2 ? 0 : xrot + 1, xb2 = xrot == 0 ? 2 : xrot - 1;
@@ -197,7 +221,7 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[2][4], uint8_t* smem, co
   // Fragments: a0/b0 = k-step 0 of the current step, a1/b1 = k-step 1.
   bf16x8 a0[2], b0[4], a1[2], b1[4];
   {
-    const uint8_t* xa = gm_xbuf(smem, xb0);
+    const uint8_t* xa = gm_xbuf<WV>(smem, xb0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       a0[i] = *reinterpret_cast<const bf16x8*>(xa + arow_off + ((lhalf ^ asw) << 4) + i * 4096);
@@ -206,9 +230,9 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[2][4], uint8_t* smem, co
       b0[j] = *reinterpret_cast<const bf16x8*>(smem + ((wn * 4 + j) * 2) * 1024 + lane * 16);
   }
   for (int kc = 0; kc < KC; ++kc) {
-    const uint8_t* xa = gm_xbuf(smem, xb0);
-    const uint8_t* xn = gm_xbuf(smem, xb1);
-    uint8_t* xc = gm_xbuf(smem, xb2);
+    const uint8_t* xa = gm_xbuf<WV>(smem, xb0);
+    const uint8_t* xn = gm_xbuf<WV>(smem, xb1);
+    uint8_t* xc = gm_xbuf<WV>(smem, xb2);
     // X pair kc+2 goes to the buffer of pair kc-1, which every wave finished
     // reading before the barrier of step 2kc-1
     const bool xto_next = kc + 2 >= KC;
@@ -249,10 +273,10 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[2][4], uint8_t* smem, co
       }
       __builtin_amdgcn_sched_barrier(0);
       // step kt+1's panel stage and X pair: this wave's copies are done when
-      // only the 6 issued after them (step kt-1's and the first half of step
-      // kt's) are outstanding, and the barrier publishes every wave's (a bare
-      // barrier: a workgroup fence would wait for every copy)
-      GM_WAIT_VM6_LGKM0();
+      // only the VM_MID issued after them (step kt-1's and the first half of
+      // step kt's) are outstanding, and the barrier publishes every wave's (a
+      // bare barrier: a workgroup fence would wait for every copy)
+      GM_WAIT_VM_LGKM0(VM_MID);
       GM_BARRIER();
       // second half: panel copies, reads of the next a0/b0, MFMAs of a1 x b1
 #pragma unroll
@@ -262,9 +286,11 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[2][4], uint8_t* smem, co
         if (g < 2) a0[g] = *reinterpret_cast<const bf16x8*>(na + arow_off + qn + g * 4096);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          if ((g & 1) == (P >> 1) && i == (P & 1)) {
+          // WC = 2: copy g / 2 at two of the slots; WC = 4: copy g in every group
+          if ((WC == 4 || (g & 1) == (P >> 1)) && i == (P & 1)) {
             __builtin_amdgcn_sched_barrier(0);
-            dma16(bk + gm_woff(g >> 1, kn), st + (wave * 2 + (g >> 1)) * 1024);
+            const int c = WC == 4 ? g : g >> 1;
+            dma16(bk + gm_woff(c, kn, ksteps), st + (wave * WC + c) * 1024);
             __builtin_amdgcn_sched_barrier(0);
           }
           acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[g], acc[i][g], 0, 0, 0);
@@ -280,14 +306,15 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[2][4], uint8_t* smem, co
 }
 
 // One tile's K loop with the wave's copy position (see the schedule above).
+template <int WV>
 __device__ __forceinline__ void gemm_tile_any(f32x16 (&acc)[2][4], uint8_t* smem,
                                               const GmSrc& cur, const GmSrc& nxt, bool has_next,
-                                              int KT, int xrot) {
+                                              int KT, int xrot, int ksteps) {
   switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
-    case 0: gemm_tile<0>(acc, smem, cur, nxt, has_next, KT, xrot); break;
-    case 1: gemm_tile<1>(acc, smem, cur, nxt, has_next, KT, xrot); break;
-    case 2: gemm_tile<2>(acc, smem, cur, nxt, has_next, KT, xrot); break;
-    default: gemm_tile<3>(acc, smem, cur, nxt, has_next, KT, xrot); break;
+    case 0: gemm_tile<WV, 0>(acc, smem, cur, nxt, has_next, KT, xrot, ksteps); break;
+    case 1: gemm_tile<WV, 1>(acc, smem, cur, nxt, has_next, KT, xrot, ksteps); break;
+    case 2: gemm_tile<WV, 2>(acc, smem, cur, nxt, has_next, KT, xrot, ksteps); break;
+    default: gemm_tile<WV, 3>(acc, smem, cur, nxt, has_next, KT, xrot, ksteps); break;
   }
 }
 
@@ -299,7 +326,7 @@ __device__ __forceinline__ void gm_drain() {
 }
 
 #undef GM_WAIT_VM
-#undef GM_WAIT_VM6_LGKM0
+#undef GM_WAIT_VM_LGKM0
 #undef GM_BARRIER
 
 }  // namespace cmp

@@ -1,9 +1,10 @@
 // Prefill: projection GEMM with the window pooling fused into its epilogue.
 //
-// Tiles are window-aligned per request.  A tile covers 256 consecutive
-// positions P0 .. P0+255 of one request (rows of x where the position is a
-// token of this call; earlier positions come from the state ring, staged by
-// prefix_kernel before the GEMM): 64 windows for ratio 4, two for ratio 128.
+// Tiles are window-aligned per request.  A tile covers BM (256, or 128 for
+// short calls) consecutive positions P0 .. P0+BM-1 of one request (rows of x
+// where the position is a token of this call; earlier positions come from
+// the state ring, staged by prefix_kernel before the GEMM): 64 (32) windows
+// for ratio 4, two (one) for ratio 128.
 // For ratio 4 (coff = 2) window w pools the first channel set of window w-1
 // and the second set of window w ([PyPTO] 压缩窗口与状态更新; [AscendC] C4A
 // 计算公式).  The first window of a request's first tile takes window w-1 from
@@ -317,9 +318,9 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
   }
 }
 
-// The copy ring takes all of LDS; the epilogue's exchange (at most 3 KiB) sits
-// in the panel stage that is idle between two tiles (GM_IDLE_OFF).
-constexpr int POOL_LDS_BYTES = GM_LDS_BYTES;
+// The copy ring takes all of the kernel's LDS; the epilogue's exchange (at
+// most 3 KiB) sits in the panel stage that is idle between two tiles
+// (GM_IDLE_OFF).
 // ratio 4: [3 row-wave boundaries][2 column waves][32 lanes]; ratio 128:
 // [2 row-wave pairs][2 column waves][64 lanes]
 static_assert(3 * 2 * 32 * sizeof(Soft) <= GM_IDLE_BYTES && 2 * 2 * 64 * sizeof(Soft) <= GM_IDLE_BYTES,
@@ -332,7 +333,7 @@ struct PoolTile {
   const int32_t* rec;
 };
 
-template <int R>
+template <int R, int BM>
 __device__ __forceinline__ PoolTile pool_tile(int tile, int tiles_n, const int32_t* __restrict__ plan,
                                               int B) {
   PoolTile t;
@@ -344,12 +345,13 @@ __device__ __forceinline__ PoolTile pool_tile(int tile, int tiles_n, const int32
   t.b = find_tile_request(plan, B, t.mt);
   t.rec = plan + (long)t.b * PL_WIDTH;
   t.tloc = t.mt - t.rec[PL_TILE0];
-  t.P0 = R * (t.rec[PL_START] / R) + t.tloc * GM_BM;
+  t.P0 = R * (t.rec[PL_START] / R) + t.tloc * BM;
   t.n0 = t.nt * GM_BN;
   return t;
 }
 
 // The tile's copy sources: X rows of positions P0 + (tile row), clamped into x.
+template <int WV>
 __device__ __forceinline__ GmSrc pool_sources(const PoolTile& t, const Cfg& cf,
                                               const uint16_t* __restrict__ X,
                                               const uint16_t* __restrict__ W, int T) {
@@ -361,18 +363,19 @@ __device__ __forceinline__ GmSrc pool_sources(const PoolTile& t, const Cfg& cf,
     const int p = t.P0 + gm_copy_row(wave, lane, j);
     arow[j] = min(max(row0 + (p - s), 0), T - 1);
   }
-  return gm_sources(X, W, cf.H, t.n0, arow, min(max(row0 + (t.P0 - s), 0), T - 1));
+  return gm_sources<WV>(X, W, cf.H, t.n0, arow, min(max(row0 + (t.P0 - s), 0), T - 1));
 }
 
 // Pooling epilogue of one tile (see the top of this file).  xch: LDS (at most
 // 3 KiB used) that no copy fills and no K loop reads while the epilogue runs.
-template <int R, int COFF>
+template <int R, int COFF, int WV>
 __device__ __forceinline__ void pool_epilogue(
     const Cfg& cf, const f32x16 (&acc)[2][4], uint8_t* xch, const PoolTile& tl,
     const float* __restrict__ ape, const float* __restrict__ staging,
     float* __restrict__ kv_state, float* __restrict__ score_state,
     const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
     float* __restrict__ pooled, int out_rows, float* __restrict__ split, uint32_t* __restrict__ err) {
+  constexpr int BM = Gm<WV>::BM, LASTWM = Gm<WV>::NWM - 1;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
@@ -397,7 +400,7 @@ __device__ __forceinline__ void pool_epilogue(
       ape_a[q] = ape[q * cD + c];
       ape_b[q] = ape[q * cD + D + c];
     }
-    if (tloc > 0 && P0 + GM_BM <= live_lo) {   // (live_lo <= e)
+    if (tloc > 0 && P0 + BM <= live_lo) {   // (live_lo <= e)
       // Interior tile: every row is a token of this call, no state row is
       // stored, window 0 is split and every other window is complete.  Group
       // statistics in two passes (max, then exp) with no per-row tests.
@@ -415,11 +418,11 @@ __device__ __forceinline__ void pool_epilogue(
       }
       // the first window of row-wave wm > 0 needs the last window of wm - 1
       Soft* xch = reinterpret_cast<Soft*>(smem);   // [wm][wn][32 lanes]
-      if (wm < 3 && h == 1) xch[(wm * 2 + wn) * 32 + lrow] = sa[7];
+      if (wm < LASTWM && h == 1) xch[(wm * 2 + wn) * 32 + lrow] = sa[7];
       __syncthreads();
       const Soft from_prev = xch[(max(wm - 1, 0) * 2 + wn) * 32 + lrow];
       float* sp = split + (size_t)mt * 6 * D;
-      if (wm == 3 && h == 1) {
+      if (wm == LASTWM && h == 1) {
         sp[0 * D + c] = sa[7].m;
         sp[1 * D + c] = sa[7].l;
         sp[2 * D + c] = sa[7].x;
@@ -488,7 +491,7 @@ __device__ __forceinline__ void pool_epilogue(
       }
     // the first window of row-wave wm > 0 needs the last window of wm - 1
     Soft* xch = reinterpret_cast<Soft*>(smem);       // [wm][wn][32 lanes]
-    if (wm < 3 && h == 1) xch[(wm * 2 + wn) * 32 + lrow] = sa[1][3];
+    if (wm < LASTWM && h == 1) xch[(wm * 2 + wn) * 32 + lrow] = sa[1][3];
     __syncthreads();
     const Soft from_prev = xch[(max(wm - 1, 0) * 2 + wn) * 32 + lrow];
     // first-set statistics of the window before the tile: staged state rows
@@ -508,7 +511,7 @@ __device__ __forceinline__ void pool_epilogue(
     // split-window statistics of this tile: [mt][a = last window's first
     // set | b = first window's second set][m, l, x][D]
     float* sp = split + (size_t)mt * 6 * D;
-    if (wm == 3 && h == 1) {
+    if (wm == LASTWM && h == 1) {
       sp[0 * D + c] = sa[1][3].m;
       sp[1 * D + c] = sa[1][3].l;
       sp[2 * D + c] = sa[1][3].x;
@@ -564,7 +567,7 @@ __device__ __forceinline__ void pool_epilogue(
     EpiCtx ctx{cf, wbase, s, e, live_lo, rec[PL_FIRST], stg, ape, c0, c1, h,
                o + wbase / R - wfirst, wfirst, wend, wbase / R,
                out_rows, pooled, smem, wm, wn};
-    if (P0 >= s && P0 + GM_BM <= live_lo) {
+    if (P0 >= s && P0 + BM <= live_lo) {
       epilogue_coff1<R, true>(ctx, acc);
     } else {
       epilogue_coff1<R, false>(ctx, acc);
@@ -602,8 +605,8 @@ __device__ __forceinline__ void pool_epilogue(
 // co-running tiles share x rows and panel slices in its L2.  While a tile
 // runs its last three K steps, the next tile's first three stages are copied,
 // so its epilogue overlaps the next tile's pipeline fill.
-template <int R, int COFF>
-__global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
+template <int R, int COFF, int WV>
+__global__ __launch_bounds__(Gm<WV>::THREADS, 1) void gemm_pool_kernel(
     Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int T, int B,
     const int32_t* __restrict__ plan, const int32_t* __restrict__ tile_count,
     const float* __restrict__ ape, const float* __restrict__ staging,
@@ -621,20 +624,20 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
   const int hi = min(lo + per_xcd, total);
   int tile = lo + (blockIdx.x >> 3);
   if (tile >= hi) return;
-  const int KT = cf.H / GM_BK;
-  PoolTile cur = pool_tile<R>(tile, tiles_n, plan, B);
-  GmSrc csrc = pool_sources(cur, cf, X, W, T);
-  gm_prologue(smem, csrc);
+  const int KT = cf.H / GM_BK, ksteps = cf.H >> 4;
+  PoolTile cur = pool_tile<R, Gm<WV>::BM>(tile, tiles_n, plan, B);
+  GmSrc csrc = pool_sources<WV>(cur, cf, X, W, T);
+  gm_prologue<WV>(smem, csrc, ksteps);
   f32x16 acc[2][4];
   const int xstep = (KT >> 1) % 3;   // X buffer rotation per tile
   int xrot = 0;
   while (true) {
     const int next = tile + per_wg;
     const bool has_next = next < hi;
-    const PoolTile nxt = has_next ? pool_tile<R>(next, tiles_n, plan, B) : cur;
-    const GmSrc nsrc = has_next ? pool_sources(nxt, cf, X, W, T) : csrc;
-    gemm_tile_any(acc, smem, csrc, nsrc, has_next, KT, xrot);
-    pool_epilogue<R, COFF>(cf, acc, xch, cur, ape, staging, kv_state, score_state, kv_tab,
+    const PoolTile nxt = has_next ? pool_tile<R, Gm<WV>::BM>(next, tiles_n, plan, B) : cur;
+    const GmSrc nsrc = has_next ? pool_sources<WV>(nxt, cf, X, W, T) : csrc;
+    gemm_tile_any<WV>(acc, smem, csrc, nsrc, has_next, KT, xrot, ksteps);
+    pool_epilogue<R, COFF, WV>(cf, acc, xch, cur, ape, staging, kv_state, score_state, kv_tab,
                            st_tab, pooled, out_rows, split, err);
     if (!has_next) break;
     tile = next;
@@ -644,7 +647,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_pool_kernel(
     // compiler from reusing the values computed before the K loop)
     cur.P0 = __builtin_amdgcn_readfirstlane(cur.P0);
     asm volatile("" : "+s"(cur.P0));
-    csrc = pool_sources(cur, cf, X, W, T);
+    csrc = pool_sources<WV>(cur, cf, X, W, T);
     xrot += xstep;
     if (xrot >= 3) xrot -= 3;
   }

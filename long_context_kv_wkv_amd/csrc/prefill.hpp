@@ -183,7 +183,10 @@ __global__ __launch_bounds__(256) void post_kernel(
       const int k = row - rrec[PL_OUT0];
       if (k < rrec[PL_NWIN]) {
         info = 1;
-        if (cf.coff == 2 && k > 0 && (k & 63) == 0) info |= 2 | ((rrec[PL_TILE0] + (k >> 6)) << 2);
+        // windows per GEMM tile: tile rows / 4 (a power of two)
+        const int wsh = __builtin_ctz(cf.bm >> 2);
+        if (cf.coff == 2 && k > 0 && (k & ((1 << wsh) - 1)) == 0)
+          info |= 2 | ((rrec[PL_TILE0] + (k >> wsh)) << 2);
       }
     }
     row_info[threadIdx.x] = info;

@@ -32,6 +32,16 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_prefill_tile_rows_setting():
+    lib = cmp.library()
+    for bad in (-1, 1, 64, 192, 512):
+        assert lib.compressor_set_prefill_tile_rows(bad) == 2          # CMP_ERR_INVALID
+    for good in (128, 256, 0):
+        assert lib.compressor_set_prefill_tile_rows(good) == 0
+    with pytest.raises(cmp.CompressorError):
+        cmp.compressor_set_prefill_tile_rows(100)
+
+
 def test_status_strings():
     assert cmp.compressor_status_str(0) == "ok"
     assert "workspace" in cmp.compressor_status_str(4)

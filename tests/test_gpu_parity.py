@@ -41,8 +41,8 @@ SMALL = ["c4li_small", "c128a_8192", "c128a_8269", "p1_comp_128", "p1_comp_4", "
 
 
 @pytest.mark.parametrize("name", SMALL)
-def test_prefill_config(harness, name):
-    _announce(name)
+def test_prefill_config(harness, name, tile_rows):
+    _announce(f"{name} tile rows {tile_rows}")
     w = workloads.build_named(name)
     case, res = _run_prefill(harness, w)
     mx, mae = assert_out(case.out_bits(), res)
@@ -79,8 +79,8 @@ def _varlen_small(seed_name, max_len, pad=0, rotate=True, B=8):
 
 
 @pytest.mark.parametrize("max_len,pad", [(700, 0), (513, 5)])
-def test_varlen_reduced(harness, max_len, pad):
-    _announce(f"varlen max_len={max_len} pad={pad}")
+def test_varlen_reduced(harness, max_len, pad, tile_rows):
+    _announce(f"varlen max_len={max_len} pad={pad} tile rows {tile_rows}")
     w = _varlen_small("varlen_small", max_len, pad)
     case, res = _run_prefill(harness, w)
     assert_out(case.out_bits(), res)

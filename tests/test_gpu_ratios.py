@@ -55,10 +55,10 @@ def _prefill_case(harness, w):
 
 
 @pytest.mark.parametrize("ratio", RATIOS)
-def test_prefill_varlen_continuation(harness, ratio):
+def test_prefill_varlen_continuation(harness, ratio, tile_rows):
     """Ragged requests continuing from state: prefix rows from the ring,
     edge and interior GEMM tiles, live state rows written back."""
-    _announce(f"prefill varlen r={ratio}")
+    _announce(f"prefill varlen r={ratio} tile rows {tile_rows}")
     w = workloads.build(_spec(f"ratio{ratio}_varlen", ratio, rotate=ratio in (2, 32)),
                         workloads.SEED_BASE + 300 + ratio)
     mx, mae = _prefill_case(harness, w)

@@ -26,7 +26,8 @@
 // Copies run three K steps ahead of the MFMAs (the X buffers: two to four):
 // on MI355X one step of MFMA work (~0.5 us) is shorter than the latency of a
 // batch of copies (~1.2 us measured), so fewer stages leave the MFMAs
-// waiting.  Each wave issues 4 copies per step, one per four MFMAs.
+// waiting.  Each wave issues 4 copies per step (6 in the 4-wave shape, which
+// copies the same panel with half as many waves).
 //
 // Workgroups are persistent (one per CU, each walking a run of tiles): the
 // last three K steps of a tile issue the copies of the first three steps of
@@ -81,7 +82,7 @@ __device__ __forceinline__ int gm_copy_row(int wave, int lane, int j) {
 }
 
 // ---------------------------------------------------------------------------
-// K loop of one 256 x 256 tile: acc[i][j] (wave (wm, wn), 32x32 block i of
+// K loop of one BM x 256 tile: acc[i][j] (wave (wm, wn), 32x32 block i of
 // its 64 rows, block j of its 128 columns) = X[rows] . Wp[n0 .. n0+256)^T.
 // K % 128 == 0 (so the K step count is a multiple of the 4 panel stages).
 //
@@ -92,8 +93,9 @@ __device__ __forceinline__ int gm_copy_row(int wave, int lane, int j) {
 // is read, and the single barrier of the step sits between the halves, so
 // no LDS read latency is exposed.  The first half issues 2 X copies (a
 // quarter of the buffer two K-step pairs ahead: step 2c issues the first
-// half of pair c+2, step 2c+1 the second), the second half the 2 panel
-// copies of step kt+3 (wave w copies column block w of the tile).  The copy
+// half of pair c+2, step 2c+1 the second), the second half the WC panel
+// copies of step kt+3 (8 waves: wave w copies column block w of the tile;
+// 4 waves: blocks 2w and 2w+1, one copy per MFMA group).  The copy
 // unit takes a 1 KiB copy every few tens of cycles and a wave cannot issue
 // past a copy it has not accepted, so waves on different SIMDs place their
 // copies at different MFMAs (P = wave % 4; other placements measured the

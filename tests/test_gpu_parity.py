@@ -120,8 +120,8 @@ def test_prefill_hadamard_matrix_kinds(harness, kind, D):
     assert case.device_error() == 0
 
 
-def test_varlen_full_sampled(harness):
-    _announce("varlen_c4a full size, sampled rows")
+def test_varlen_full_sampled(harness, tile_rows):
+    _announce(f"varlen_c4a full size, sampled rows, tile rows {tile_rows}")
     w = workloads.build_named("varlen_c4a")
     plan = O.make_plan(4, w["batch"], w["T"], w["cu_seqlens"], w["seqused"], w["start_pos"])
     rng = np.random.default_rng(5)
@@ -131,6 +131,8 @@ def test_varlen_full_sampled(harness):
         o = int(plan.out0[b])
         rows.update([o, o + u - 1] if u else [])
         rows.update(int(v) for v in o + rng.integers(0, max(u, 1), 6) if u)
+        # windows split between two 128-row (32 windows) or 256-row tiles
+        rows.update(int(v) for v in o + 32 * rng.integers(1, max(u // 32, 1) + 1, 4) if v < o + u)
     rows.update(int(v) for v in rng.integers(0, w["out_rows"], 16))
     case, res = _run_prefill(harness, w, rows=rows, project_all=False)
     assert_out(case.out_bits(), res, rows=rows)
@@ -139,11 +141,12 @@ def test_varlen_full_sampled(harness):
     assert case.device_error() == 0
 
 
-def test_c4a_128k_sampled(harness):
-    _announce("c4a_128k full size, sampled rows")
+def test_c4a_128k_sampled(harness, tile_rows):
+    _announce(f"c4a_128k full size, sampled rows, tile rows {tile_rows}")
     w = workloads.build_named("c4a_128k")
     rng = np.random.default_rng(6)
-    rows = {0, 1, 2, 63, 64, 32767} | set(int(v) for v in rng.integers(0, 32768, 40))
+    rows = ({0, 1, 2, 31, 32, 33, 63, 64, 32736, 32767}
+            | set(int(v) for v in rng.integers(0, 32768, 40)))
     case, res = _run_prefill(harness, w, rows=rows, project_all=False)
     mx, mae = assert_out(case.out_bits(), res, rows=rows)
     kv, sc = case.states()

@@ -269,6 +269,41 @@ def test_determinism_bitwise(harness):
     assert np.array_equal(a, d.out_bits())
 
 
+@pytest.mark.parametrize("name,exact", [("c128a_8269", True), ("varlen_c4a", False)])
+def test_tile_heights_agree(harness, name, exact):
+    """The same call with 128-row and 256-row projection tiles.  The state
+    rows come straight from the accumulators, whose K order does not depend
+    on the tile height: bit-identical.  At ratio 128 every window lies in
+    one tile at either height and is pooled by the same code: outputs
+    bit-identical.  At ratio 4 the windows split between two tiles differ
+    with the height (merged by the post kernel instead of in the epilogue):
+    outputs within the output tolerance of each other."""
+    import long_context_kv_wkv_amd as cmp
+    _announce(f"tile heights agree: {name}")
+    got = []
+    for rows in (128, 256):
+        cmp.compressor_set_prefill_tile_rows(rows)
+        try:
+            case = harness.DeviceCase(workloads.build_named(name))
+            case.prefill()
+            torch.cuda.synchronize()
+            assert case.device_error() == 0
+            got.append((case.out_bits().copy(), case.states()))
+        finally:
+            cmp.compressor_set_prefill_tile_rows(0)
+    (o1, (k1, s1)), (o2, (k2, s2)) = got
+    assert np.array_equal(k1.view(np.uint32), k2.view(np.uint32))
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    if exact:
+        assert np.array_equal(o1, o2)
+    else:
+        a, g = O.bf16_to_f64(o1), O.bf16_to_f64(o2)
+        rms = np.sqrt(np.mean(a * a, axis=1, keepdims=True))
+        worst = float(np.max(np.abs(a - g) / np.maximum(np.maximum(np.abs(a), rms), 1e-30)))
+        print(f"{name}: {int((o1 != o2).any(axis=1).sum())} rows differ, max scaled {worst:.2e}")
+        assert worst <= 2e-2, worst
+
+
 @pytest.mark.parametrize("rotate", [True, False])
 def test_prefill_equals_token_by_token_decode(harness, rotate):
     """Config-4 style: packed varlen prefill vs the same tokens fed one per

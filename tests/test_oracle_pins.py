@@ -416,3 +416,115 @@ def test_ratio_one_reduces_to_linear_plus_rmsnorm():
     ref = torch.nn.functional.rms_norm(lin, (D,), torch.from_numpy(O.bf16_to_f64(w["weight"])),
                                        eps=1e-6).numpy()
     assert np.allclose(res.out[:T], ref, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# where RoPE and the Hadamard product act, through the whole call
+# --------------------------------------------------------------------------
+def _uniform_windows(ratio, D, H, T, seed, **kw):
+    """Inputs with Wgate = 0, Ape = 0 and weight 1, so that window k's pooled
+    vector is the plain mean of its slots' kv, and the RMS-normalised means
+    y_k (projection by explicit sums, pooling by plain means, RMSNorm by its
+    closed form): everything the output holds before RoPE and the Hadamard
+    product."""
+    rng = np.random.default_rng(seed)
+    coff = O.coff_of(ratio)
+    w = make_inputs(ratio=ratio, D=D, H=H, x=rng.standard_normal((T, H)),
+                    wkv=rng.standard_normal((coff * D, H)), wgate=np.zeros((coff * D, H)),
+                    ape=np.zeros((ratio, coff * D)), lengths=[T], **kw)
+    xb, wb = O.bf16_to_f64(w["x"]), O.bf16_to_f64(w["wkv"])
+    kv = np.array([[math.fsum(xb[p, h] * wb[c, h] for h in range(H)) for c in range(coff * D)]
+                   for p in range(T)])
+    ys = []
+    for k in range(T // ratio):
+        if coff == 1:
+            c = kv[k * ratio:(k + 1) * ratio].mean(0)
+        elif k == 0:
+            c = kv[0:4, D:].mean(0)
+        else:
+            c = np.concatenate([kv[(k - 1) * 4:k * 4, :D], kv[k * 4:(k + 1) * 4, D:]]).mean(0)
+        ys.append(c / math.sqrt(np.mean(c * c) + 1e-6))
+    return w, ys
+
+
+@pytest.mark.parametrize("ratio", [4, 128])
+def test_rope_acts_on_the_trailing_slice_only(ratio):
+    """Every pair of the rotary slice turned by a quarter turn (cos 0, sin 1,
+    exact in bf16): channels [0, D-64) keep their values and the trailing
+    pairs (D-64+2i, D-64+2i+1) become (-odd, even) ([PyPTO]
+    数值精度与验证要点: RoPE on the last rope_head_dim channels)."""
+    D, H = 128, 12
+    T = 3 * ratio
+    rows = T // ratio + 1
+    w, ys = _uniform_windows(ratio, D, H, T, 12, cos=np.zeros((rows, 64)),
+                             sin=np.ones((rows, 64)), out_rows=rows)
+    res = O.compressor(w)
+    for k, y in enumerate(ys):
+        want = y.copy()
+        want[D - 64::2] = -y[D - 63::2]
+        want[D - 63::2] = y[D - 64::2]
+        assert np.allclose(res.out[k], want, rtol=1e-12, atol=1e-12), k
+        assert np.array_equal(res.out[k][:D - 64], y[:D - 64])
+
+
+def test_rope_row_angles_against_complex_rotation_in_pipeline():
+    """Row-dependent angles: output row k rotates pair i of the trailing
+    slice by its own angle theta[k, i] (the complex product of
+    (y[D-64+2i] + j y[D-64+2i+1]) with e^{j theta}, computed by torch), and
+    channels below the slice are untouched."""
+    D, H, r, T = 128, 10, 4, 20
+    rows = T // r + 1
+    rng = np.random.default_rng(13)
+    theta = rng.uniform(-3, 3, (rows, 32))
+    cos = O.bf16_to_f64(bf(np.concatenate([np.cos(theta)] * 2, -1)))
+    sin = O.bf16_to_f64(bf(np.concatenate([np.sin(theta)] * 2, -1)))
+    w, ys = _uniform_windows(r, D, H, T, 14, cos=cos, sin=sin, out_rows=rows)
+    res = O.compressor(w)
+    for k, y in enumerate(ys):
+        c, s = torch.from_numpy(cos[k, :32]), torch.from_numpy(sin[k, :32])
+        z = torch.view_as_complex(torch.from_numpy(y[D - 64:]).reshape(32, 2).contiguous())
+        rot = torch.view_as_real(z * torch.complex(c, s)).reshape(64).numpy()
+        want = np.concatenate([y[:D - 64], rot])
+        assert np.allclose(res.out[k], want, rtol=1e-12, atol=1e-12), k
+
+
+def test_hadamard_product_orientation():
+    """out = y @ Had ([PyPTO] kernel 派发逻辑), checked with matrices that are
+    not symmetric: the upper triangular all-ones matrix U (y @ U is the
+    running sum of y, y @ U^T the running sum from the end) and a
+    permutation matrix P with P[k, perm[k]] = 1 (y @ P moves channel k to
+    perm[k])."""
+    rng = np.random.default_rng(15)
+    y = rng.standard_normal((3, 64))
+    U = np.triu(np.ones((64, 64)))
+    assert np.allclose(O.hadamard_rotate(y, U), np.cumsum(y, axis=-1), rtol=1e-13, atol=1e-13)
+    perm = rng.permutation(64)
+    P = np.zeros((64, 64))
+    P[np.arange(64), perm] = 1.0
+    got = O.hadamard_rotate(y, P)
+    assert np.array_equal(got[:, perm], y)
+
+
+@pytest.mark.parametrize("ratio", [4, 128])
+def test_hadamard_orientation_in_pipeline(ratio):
+    """rotate with the upper triangular all-ones matrix (exact in bf16):
+    every output row is the running sum of its normalised vector."""
+    D, H = 128, 9
+    T = 2 * ratio + 3
+    w, ys = _uniform_windows(ratio, D, H, T, 16, had=np.triu(np.ones((D, D))))
+    res = O.compressor(w)
+    for k, y in enumerate(ys):
+        assert np.allclose(res.out[k], np.cumsum(y), rtol=1e-11, atol=1e-11), k
+
+
+def test_f32_state_rounding():
+    """States are rounded once from fp64 to fp32, nearest-even: against
+    torch's own conversion, and at ties."""
+    rng = np.random.default_rng(17)
+    v = rng.standard_normal(100000) * np.exp(rng.uniform(-60, 60, 100000))
+    ref = torch.from_numpy(v).to(torch.float32).numpy()
+    assert np.array_equal(O.f64_to_f32(v).view(np.uint32), ref.view(np.uint32))
+    e = 2.0 ** -24                         # half an fp32 ulp at 1
+    assert O.f64_to_f32(1 + e) == np.float32(1.0)
+    assert O.f64_to_f32(1 + 3 * e) == np.float32(1 + 4 * e)
+    assert O.f64_to_f32(1 + e + 2.0 ** -50) == np.float32(1 + 2 * e)

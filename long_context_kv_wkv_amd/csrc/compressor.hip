@@ -170,18 +170,26 @@ int prefill_max_tiles(int T, int B, int bm) {
   return (T + bm - 1) / bm + 2 * B;
 }
 
-// decode split: K ranges per 32-column block so that about 256+ workgroups
-// stream the panel; each wave's share is a whole number of 8-step (128-k) runs
-int decode_ksplit(const Cfg& cf) {
-  const int cblocks = cf.N / 32;
-  const int units = cf.H / (128 * (GV_THREADS / 64));   // 8-step runs per wave x 8 waves
-  int best = 1;
-  for (int ks = 1; ks <= units; ++ks) {
-    if (units % ks) continue;
-    best = ks;
-    if (cblocks * ks >= 256) break;
-  }
-  return best;
+// decode split: KS K ranges per 32-column block, for about 512 GEMV
+// workgroups (two per CU) with 4 to 8 k-steps per wave (8 waves per range;
+// dec_wave_range cuts the H / 16 k-steps into 8 * KS nearly equal parts, so
+// no part of K is left out for any H).  KS <= H / 512 <= DEC_MAX_KSPLIT.
+int decode_ksplit(const Cfg& cf, int side_wgs) {
+  const int ncb = cf.N / 32, KT = cf.H / 16;
+  // workgroups beside the GEMV (pre-pooling) hold CU slots too:
+  // with 64 KiB of LDS two workgroups fit a CU, and a GEMV workgroup that
+  // finds no slot runs as a second wave
+  const int budget = std::max(ncb, 512 - side_wgs);
+  int ks = std::max(1, budget / ncb);
+  ks = std::max(ks, (KT + 63) / 64);        // at most 8 k-steps per wave
+  ks = std::min(ks, KT / 32);               // at least 4 k-steps per wave
+  return std::max(1, std::min(ks, DEC_MAX_KSPLIT));
+}
+// k-steps of the longest wave range, and the run length that covers it
+int decode_run(const Cfg& cf, int ks, int nrb) {
+  const int KT = cf.H / 16;
+  const int steps = (KT + 8 * ks - 1) / (8 * ks);
+  return nrb == 2 || steps <= 4 ? 4 : 8;
 }
 
 constexpr int kDecodeMaxBatch = 64;
@@ -193,7 +201,7 @@ struct DecodeLayout {
 };
 DecodeLayout decode_layout(const Cfg& cf, int B) {
   DecodeLayout L;
-  L.ks = decode_ksplit(cf);
+  L.ks = decode_ksplit(cf, 0);             // the most K ranges any call uses
   with_ratio(cf.ratio, [&]<int R>() { L.split = dec_split<R>(); });
   size_t o = 0;
   L.err = o;       o += 256;
@@ -326,18 +334,20 @@ int compressor_state_init(const compressor_shape* shape, float* kv_state, float*
 
 int compressor_state_reset(const compressor_shape* shape, float* kv_state, float* score_state,
                            const int32_t* kv_block_table, const int32_t* state_block_table,
-                           const int32_t* rows, int32_t n, void* stream) {
+                           const int32_t* rows, int32_t n, int32_t table_rows,
+                           uint32_t* device_error, void* stream) {
   Cfg cf;
   CMP_TRY(check_shape(shape, &cf));
   if (n < 0) return CMP_ERR_INVALID;
   if (n == 0) return CMP_OK;
+  if (table_rows < 1) return CMP_ERR_INVALID;
   if (!kv_state || !score_state || !state_block_table || !rows) return CMP_ERR_NULLPTR;
   const int32_t* kvt = kv_block_table ? kv_block_table : state_block_table;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int used = (cf.coff * cf.ratio + cf.bs - 1) / cf.bs;
   return launch("state_fill", st, [&] {
     hipLaunchKernelGGL(reset_rows_kernel, dim3(used, n), dim3(256), 0, st, cf, kv_state,
-                       score_state, kvt, state_block_table, rows);
+                       score_state, kvt, state_block_table, rows, table_rows, device_error);
   });
 }
 
@@ -439,52 +449,57 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
   DecRec* rec = reinterpret_cast<DecRec*>(ws + L.rec);
   const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
   const int B = a->batch;
-  const int steps = cf.H / 16 / (L.ks * (GV_THREADS / 64));
   const int T = a->T;
+  const uint16_t* cosv = static_cast<const uint16_t*>(a->cos);
+  const uint16_t* sinv = static_cast<const uint16_t*>(a->sin);
   // the most windows a request can complete: its tokens (one without
   // cu_seqlens, else at most 4 and at most T) span ceil(tokens / ratio)
   const int max_tok = a->cu_seqlens ? std::min(T, DEC_MAX_TOK) : 1;
   const int nwin = std::max(1, std::min(DEC_MAX_WIN, (max_tok + cf.ratio - 1) / cf.ratio));
-  const dim3 gg(B * nwin * L.split + cf.N / 32 * L.ks);
+  const int side = B * nwin * L.split;
+  const int ks = decode_ksplit(cf, side);
+  const dim3 gg(side + cf.N / 32 * ks);
+  const int nrb = T <= 32 ? 1 : 2;
+  const int run = decode_run(cf, ks, nrb);
   CMP_TRY(launch("decode_main", st, [&] {
     const uint16_t* X = static_cast<const uint16_t*>(a->x);
     const uint16_t* W = static_cast<const uint16_t*>(a->w_packed);
-    decltype(&decode_main_kernel<1, 4, 2>) kern = nullptr;
+    decltype(&decode_main_kernel<1, 8, 4, 2>) kern = nullptr;
     with_ratio(cf.ratio, [&]<int R>() {
-      kern = T <= 32 ? decode_main_kernel<1, R, coff_of<R>()> : decode_main_kernel<2, R, coff_of<R>()>;
+      constexpr int C = coff_of<R>();
+      kern = nrb == 2 ? decode_main_kernel<2, 4, R, C>
+                      : (run == 8 ? decode_main_kernel<1, 8, R, C> : decode_main_kernel<1, 4, R, C>);
     });
-    hipLaunchKernelGGL(kern, gg, dim3(GV_THREADS), 0, st, cf, X, W, partial, B, T, nwin, steps,
+    hipLaunchKernelGGL(kern, gg, dim3(GV_THREADS), 0, st, cf, X, W, partial, B, T, nwin, ks,
                        a->cu_seqlens, a->seqused, a->start_pos, a->kv_state, a->score_state, kvt,
                        a->state_block_table, pp, ppflag, rec, err);
   }));
   return launch("decode_tail", st, [&] {
     const uint16_t* gamma = static_cast<const uint16_t*>(a->norm_weight);
-    const uint16_t* cosv = static_cast<const uint16_t*>(a->cos);
-    const uint16_t* sinv = static_cast<const uint16_t*>(a->sin);
     const uint16_t* had = static_cast<const uint16_t*>(a->hadamard);
     uint16_t* out = static_cast<uint16_t*>(a->out);
     if (a->cu_seqlens) {
       decltype(&decode_tail_kernel<4, 2, 8>) tail = nullptr;
       with_ratio(cf.ratio, [&]<int R>() {
         constexpr int C = coff_of<R>();
-        tail = L.ks <= 8 ? decode_tail_kernel<R, C, 8>
-                         : (L.ks <= 16 ? decode_tail_kernel<R, C, 16>
+        tail = ks <= 8 ? decode_tail_kernel<R, C, 8>
+                         : (ks <= 16 ? decode_tail_kernel<R, C, 16>
                                        : decode_tail_kernel<R, C, DEC_MAX_KSPLIT>);
       });
-      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, L.ks, B, T,
+      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, ks, B, T,
                          a->cu_seqlens, a->seqused, a->start_pos, a->ape, a->kv_state,
                          a->score_state, kvt, a->state_block_table, pp, ppflag, gamma, cosv,
                          sinv, had, out, a->out_rows, err);
     } else {
-      // the tail loads a fixed number of K ranges (>= L.ks, <= DEC_MAX_KSPLIT)
+      // the tail loads a fixed number of K ranges (>= ks, <= DEC_MAX_KSPLIT)
       decltype(&decode_tail1_kernel<4, 2, 8>) tail = nullptr;
       with_ratio(cf.ratio, [&]<int R>() {
         constexpr int C = coff_of<R>();
-        tail = L.ks <= 8 ? decode_tail1_kernel<R, C, 8>
-                         : (L.ks <= 16 ? decode_tail1_kernel<R, C, 16>
+        tail = ks <= 8 ? decode_tail1_kernel<R, C, 8>
+                         : (ks <= 16 ? decode_tail1_kernel<R, C, 16>
                                        : decode_tail1_kernel<R, C, DEC_MAX_KSPLIT>);
       });
-      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, L.ks, B, rec,
+      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, ks, B, rec,
                          a->ape, a->kv_state, a->score_state, pp, ppflag, gamma, cosv, sinv, had,
                          out, a->out_rows, err);
     }

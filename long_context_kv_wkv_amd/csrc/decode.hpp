@@ -9,6 +9,15 @@
 // waves reduce through LDS and the workgroup writes one fp32 partial per K
 // range; the tail kernel sums the K ranges in a fixed order (deterministic).
 //
+// The K split: the H/16 k-steps are cut into 8 * KS nearly equal wave ranges
+// (KS K ranges of 8 waves), so any H that is a multiple of 512 is covered
+// whole; KS is chosen for about 512 GEMV workgroups (two per CU) with 4 to 8
+// k-steps per wave.  All of a wave's loads are issued before its first MFMA:
+// with more loads in flight per wave than one round of HBM latency covers,
+// a second round per wave only adds its latency (measured: 7 steps per wave
+// over 512 workgroups streams the 29 MB C4A panel in 8.5 us of graph time
+// against 9.0 us for 8 steps over 448).
+//
 // The Triton-Ascend article (性能优化 / Decode) made the same observation for
 // its hardware: decode must split along output columns and use a larger K
 // step per loop so that more cores take part.
@@ -22,19 +31,21 @@ constexpr int GV_THREADS = 512;                // 8 waves
 typedef __attribute__((address_space(3))) void dec_lds_t;
 typedef __attribute__((address_space(1))) void dec_glb_t;
 
-// One run of U k16-steps of a wave.  The x rows of the run go to the wave's
-// own LDS region by direct-to-LDS copies that each cover whole 16-byte-chunk
-// runs of rows (a row of the run is U*32 contiguous bytes), then the panel
-// fragments of the run are loaded (1 KiB contiguous each); once the copies
-// have landed, the x fragments are read from LDS and the MFMAs run.  Row t,
-// chunk c sits at t*U*32 + ((c ^ (t & m)) * 16), m = min(2U, 16) - 1 (the
-// swizzle never leaves the row's 2U chunks): the fragment reads (32 rows at
-// one chunk index) spread over the banks.  Rows >= B repeat row
-// B-1 (their results are not used).
+// One run of U k16-steps of a wave, steps s .. s+U-1 of its n (steps at or
+// beyond n load step n-1 again and skip their MFMA, so every run issues the
+// same number of loads).  The x rows of the run go to the wave's own LDS
+// region by direct-to-LDS copies that each cover whole 16-byte-chunk runs of
+// rows (a row of the run is U*32 contiguous bytes), then the panel fragments
+// of the run are loaded (1 KiB contiguous each); once the copies have
+// landed, the x fragments are read from LDS and the MFMAs run.  Row t, chunk
+// c sits at t*U*32 + ((c ^ (t & m)) * 16), m = min(2U, 16) - 1 (the swizzle
+// never leaves the row's 2U chunks): the fragment reads (32 rows at one
+// chunk index) spread over the banks.  Rows >= B repeat row B-1 (their
+// results are not used).
 template <int U, int NRB>
 __device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp,
                                          const uint16_t* __restrict__ xk, int K, int B, int s,
-                                         uint8_t* xl, f32x16* acc) {
+                                         int n, uint8_t* xl, f32x16* acc) {
   constexpr int CPR = 2 * U;             // 16-byte chunks per row of the run
   constexpr int RPI = 64 / CPR;          // rows per copy instruction
   constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;   // chunk swizzle mask: stays inside the row
@@ -44,27 +55,43 @@ __device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp,
   for (int j = 0; j < NRB * U; ++j) {
     const int t = j * RPI + lane / CPR;
     const int c = (lane % CPR) ^ (t & SWZ);
-    __builtin_amdgcn_global_load_lds((dec_glb_t*)(xk + (size_t)min(t, B - 1) * K + s * 16 + c * 8),
-                                     (dec_lds_t*)(xl + j * 1024), 16, 0, 0);
+    const int ks = min(s + (c >> 1), n - 1);
+    __builtin_amdgcn_global_load_lds(
+        (dec_glb_t*)(xk + (size_t)min(t, B - 1) * K + ks * 16 + (c & 1) * 8),
+        (dec_lds_t*)(xl + j * 1024), 16, 0, 0);
   }
   bf16x8 wf[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8*>(wp + (s + u) * 512);
+  for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8*>(wp + min(s + u, n - 1) * 512);
   // the copies were issued first: when only the U panel loads are
   // outstanding, they have landed
   __builtin_amdgcn_s_waitcnt((U & 0xf) | ((U >> 4) << 14) | 0x0f70);
   __builtin_amdgcn_sched_barrier(0);
+  // every MFMA runs (a branch around the steps past n would let the compiler
+  // sink their panel loads into it, one round trip at a time); those steps
+  // multiply a zero x fragment
+  const bf16x8 zero = {};
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u) {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int t = rb * 32 + (lane & 31);
       const int c = 2 * u + (lane >> 5);
-      const bf16x8 xf = *reinterpret_cast<const bf16x8*>(xl + t * CPR * 16 + ((c ^ (t & SWZ)) << 4));
+      bf16x8 xf = *reinterpret_cast<const bf16x8*>(xl + t * CPR * 16 + ((c ^ (t & SWZ)) << 4));
+      xf = s + u < n ? xf : zero;
       acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, wf[u], acc[rb], 0, 0, 0);
     }
+  }
   // the next run's copies overwrite the region: every read must be done
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+}
+
+// K range [k0, k1) of wave range v of 8 * KS: nearly equal shares of the KT
+// k-steps (lengths differ by at most one).
+__host__ __device__ __forceinline__ void dec_wave_range(int v, int KS, int KT, int* k0, int* k1) {
+  const int nr = 8 * KS;                // v * KT <= 8 * 20 * 640: no overflow
+  *k0 = v * KT / nr;
+  *k1 = (v + 1) * KT / nr;
 }
 
 // ---------------------------------------------------------------------------
@@ -230,15 +257,16 @@ __device__ __forceinline__ void dec_records(const Cfg& cf, int B, const int32_t*
 
 // Decode main kernel.  Workgroups [0, B * nwin * split) pre-pool ring windows
 // (prepool_block; nwin <= DEC_MAX_WIN is the most windows a request can
-// complete in this call); the rest run the GEMV over the T packed rows:
-// workgroup g owns column block g % (N / 32) and K range g / (N / 32), its 8
-// waves divide the range, reduce through LDS in a fixed order and write one
-// fp32 partial per K range.  With one row per request (cu NULL), workgroup 0
-// also writes the request records.
-template <int NRB, int R, int COFF>
+// complete in this call); with one row per request (cu NULL) workgroup 0
+// also writes the request records.  The rest run the GEMV over the T packed
+// rows: workgroup g owns column block g % (N / 32) and K range kr =
+// g / (N / 32); wave w covers wave range 8 kr + w (dec_wave_range) in runs of
+// RUN k-steps; the 8 waves reduce through LDS in a fixed order and the
+// workgroup writes one fp32 partial per K range.
+template <int NRB, int RUN, int R, int COFF>
 __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
     Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
-    float* __restrict__ partial, int B, int T, int nwin, int steps_per_wave,
+    float* __restrict__ partial, int B, int T, int nwin, int KS,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seqused,
     const int32_t* __restrict__ start_pos,
     const float* __restrict__ kv_state, const float* __restrict__ score_state,
@@ -246,7 +274,7 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
     float* __restrict__ pp, int32_t* __restrict__ ppflag, DecRec* __restrict__ rec,
     uint32_t* __restrict__ err) {
   // per wave: the x rows of a run, then (after the runs) its accumulators
-  constexpr int RUN = 8 / NRB;                   // k-steps per run: 8 KiB of x per wave
+  static_assert(NRB * 32 * RUN * 32 >= NRB * 16 * 64 * 4, "the reduction fits the x region");
   __shared__ __attribute__((aligned(1024))) uint8_t xstage[GV_THREADS / 64][NRB * 32 * RUN * 32];
   constexpr int NSPLIT = dec_split<R>();
   const int npre = B * nwin * NSPLIT;
@@ -260,16 +288,19 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
     return;
   }
   const int g = blockIdx.x - npre;
-  const int N = cf.N, K = cf.H;
+  const int N = cf.N, K = cf.H, KT = K >> 4;
   const int ncb = N / 32;
   const int cb = g % ncb, kr = g / ncb;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
   if (g == 0 && tid == 0) *err = 0;   // this call's error word (only the tail sets bits)
   if (T == 0) return;
-  const int kstep0 = (kr * (GV_THREADS / 64) + wave) * steps_per_wave;
-  // fragment (column block cb, k-step kstep0 + u) is 1 KiB contiguous
-  const uint16_t* wp = W + (((size_t)cb * (K >> 4) + kstep0) * 64 + lane) * 8;
-  const uint16_t* xk = X + (size_t)kstep0 * 16;
+  int k0, k1;
+  dec_wave_range(kr * (GV_THREADS / 64) + wave, KS, KT, &k0, &k1);
+  const int n = k1 - k0;
+  // fragment (column block cb, k-step k0 + u) is 1 KiB contiguous
+  const uint16_t* wp = W + (((size_t)cb * KT + k0) * 64 + lane) * 8;
+  const uint16_t* xk = X + (size_t)k0 * 16;
   uint8_t* xl = xstage[wave];
 
   f32x16 acc[NRB];
@@ -278,9 +309,7 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[rb][r] = 0.f;
 
-  int s = 0;
-  // (every wave's share is a multiple of 8 k-steps)
-  for (; s + RUN <= steps_per_wave; s += RUN) gemv_run<RUN, NRB>(wp, xk, K, T, s, xl, acc);
+  for (int s = 0; s < n; s += RUN) gemv_run<RUN, NRB>(wp, xk, K, T, s, n, xl, acc);
   float* red = reinterpret_cast<float*>(xl);            // [NRB * 16][64] of this wave
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)

@@ -177,12 +177,25 @@ int compressor_pack_weights(const compressor_shape* shape, const void* wkv, cons
 int compressor_state_init(const compressor_shape* shape, float* kv_state, float* score_state,
                           void* stream);
 
-/* Reset the ring blocks of n requests: rows (device, int32 [n]) are
- * block-table row indices; every block those table rows name (first
- * ceil(coff*r / block_size) entries) is refilled with kv 0 / score -inf. */
+/* Reset the ring blocks of n requests to kv 0 / score -inf.
+ * kv_block_table, state_block_table  (device) int32 [table_rows, table_stride]
+ *                 (kv_block_table NULL: state_block_table for both pools).
+ * rows            (device) int32 [n]: table rows to reset; for each, every
+ *                 block its first ceil(coff*r / block_size) entries name is
+ *                 refilled (kv_state through kv_block_table, score_state
+ *                 through state_block_table).  Blocks no listed row names
+ *                 keep their contents.
+ * table_rows      rows of the tables (>= 1 when n > 0).
+ * device_error    (device) uint32 word, may be NULL: a row index outside
+ *                 [0, table_rows) or a table entry outside [0, num_blocks)
+ *                 is skipped (no access through it) and ORs CMP_DEVERR_TABLE
+ *                 into it (the caller clears the word).
+ * Returns CMP_OK (n == 0: nothing is enqueued), CMP_ERR_NULLPTR,
+ * CMP_ERR_INVALID (n < 0 or table_rows < 1) or CMP_ERR_HIP. */
 int compressor_state_reset(const compressor_shape* shape, float* kv_state, float* score_state,
                            const int32_t* kv_block_table, const int32_t* state_block_table,
-                           const int32_t* rows, int32_t n, void* stream);
+                           const int32_t* rows, int32_t n, int32_t table_rows,
+                           uint32_t* device_error, void* stream);
 
 /* One Compressor call over packed variable-length requests ([CANN] 接口功能
  * and 计算公式; [PyPTO] 压缩窗口与状态更新; [Triton] 流式调用).  Computes the

@@ -94,7 +94,7 @@ def library():
             "compressor_decode_workspace_size": (sp, i32, i32, ctypes.POINTER(sz)),
             "compressor_pack_weights": (sp, vp, vp, vp, vp),
             "compressor_state_init": (sp, vp, vp, vp),
-            "compressor_state_reset": (sp, vp, vp, vp, vp, vp, i32, vp),
+            "compressor_state_reset": (sp, vp, vp, vp, vp, vp, i32, i32, vp, vp),
             "compressor_prefill": (sp, ap, vp),
             "compressor_decode": (sp, ap, vp),
             "compressor_last_device_error": (vp, vp, ctypes.POINTER(i32)),
@@ -180,12 +180,17 @@ def compressor_state_init(shape: Shape, kv_state: torch.Tensor, score_state: tor
 
 
 def compressor_state_reset(shape: Shape, kv_state, score_state, kv_block_table,
-                           state_block_table, rows: torch.Tensor, stream=None) -> None:
+                           state_block_table, rows: torch.Tensor, device_error=None,
+                           stream=None) -> None:
+    """Refill with kv 0 / score -inf every ring block that table rows `rows`
+    name; device_error (int32 [1], optional) receives CMP_DEVERR_TABLE for
+    a row or table entry out of range (skipped)."""
     f, i = torch.float32, torch.int32
     _check("compressor_state_reset", library().compressor_state_reset(
         ctypes.byref(shape), _dev(kv_state, f, "kv_state"), _dev(score_state, f, "score_state"),
         _dev(kv_block_table, i, "kv_block_table"), _dev(state_block_table, i, "state_block_table"),
-        _dev(rows, i, "rows"), int(rows.numel()), _stream(stream)))
+        _dev(rows, i, "rows"), int(rows.numel()), int(state_block_table.shape[0]),
+        _dev(device_error, i, "device_error"), _stream(stream)))
 
 
 def make_args(*, x, batch, kv_state, score_state, state_block_table, w_packed, ape, norm_weight,

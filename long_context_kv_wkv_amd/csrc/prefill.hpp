@@ -448,20 +448,27 @@ __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, long n
 }
 
 // Refill the ring blocks named by table rows rows[0..n): kv 0, score -inf.
+// Workgroup (j, i) refills entry j of table row rows[i]; a row index outside
+// [0, table_rows) or an entry outside [0, num_blocks) is skipped and reported.
 __global__ __launch_bounds__(256) void reset_rows_kernel(Cfg cf, float* __restrict__ kv_state,
                                                         float* __restrict__ score_state,
                                                         const int32_t* __restrict__ kv_tab,
                                                         const int32_t* __restrict__ st_tab,
-                                                        const int32_t* __restrict__ rows) {
+                                                        const int32_t* __restrict__ rows,
+                                                        int table_rows, uint32_t* __restrict__ err) {
   const int rb = rows[blockIdx.y];
-  const int used = (cf.coff * cf.ratio + cf.bs - 1) / cf.bs;
   const int j = blockIdx.x;
-  if (j >= used) return;
+  if (rb < 0 || rb >= table_rows) {
+    if (j == 0 && threadIdx.x == 0 && err) atomicOr(err, CMP_DEVERR_TABLE);
+    return;
+  }
   const int kb = kv_tab[(long)rb * cf.stride + j], sb = st_tab[(long)rb * cf.stride + j];
+  const bool kok = kb >= 0 && kb < cf.nblocks, sok = sb >= 0 && sb < cf.nblocks;
+  if ((!kok || !sok) && threadIdx.x == 0 && err) atomicOr(err, CMP_DEVERR_TABLE);
   const long blk = (long)cf.bs * cf.coff * cf.D;
-  if (kb >= 0 && kb < cf.nblocks)
+  if (kok)
     for (long i = threadIdx.x; i < blk; i += blockDim.x) kv_state[kb * blk + i] = 0.f;
-  if (sb >= 0 && sb < cf.nblocks)
+  if (sok)
     for (long i = threadIdx.x; i < blk; i += blockDim.x) score_state[sb * blk + i] = -INFINITY;
 }
 

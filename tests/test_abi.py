@@ -89,7 +89,11 @@ def test_null_arguments_rejected_before_any_launch():
     assert lib.compressor_prefill(ctypes.byref(sh), ctypes.byref(args), None) == 1
     assert lib.compressor_pack_weights(ctypes.byref(sh), None, None, None, None) == 1
     assert lib.compressor_state_init(ctypes.byref(sh), None, None, None) == 1
-    assert lib.compressor_state_reset(ctypes.byref(sh), None, None, None, None, None, 0, None) == 0
+    reset = lib.compressor_state_reset
+    assert reset(ctypes.byref(sh), None, None, None, None, None, 0, 0, None, None) == 0   # n == 0
+    assert reset(ctypes.byref(sh), None, None, None, None, None, -1, 4, None, None) == 2
+    assert reset(ctypes.byref(sh), None, None, None, None, None, 2, 0, None, None) == 2  # no table rows
+    assert reset(ctypes.byref(sh), None, None, None, None, None, 2, 4, None, None) == 1
     code = ctypes.c_int32()
     assert lib.compressor_last_device_error(None, None, ctypes.byref(code)) == 1
     n = ctypes.c_int32()

@@ -120,39 +120,37 @@ def test_prefill_hadamard_matrix_kinds(harness, kind, D):
     assert case.device_error() == 0
 
 
-def test_varlen_full_sampled(harness, tile_rows):
-    _announce(f"varlen_c4a full size, sampled rows, tile rows {tile_rows}")
-    w = workloads.build_named("varlen_c4a")
-    plan = O.make_plan(4, w["batch"], w["T"], w["cu_seqlens"], w["seqused"], w["start_pos"])
-    rng = np.random.default_rng(5)
-    rows = set()
-    for b in range(w["batch"]):
-        u = int(plan.nrows[b])
-        o = int(plan.out0[b])
-        rows.update([o, o + u - 1] if u else [])
-        rows.update(int(v) for v in o + rng.integers(0, max(u, 1), 6) if u)
-        # windows split between two 128-row (32 windows) or 256-row tiles
-        rows.update(int(v) for v in o + 32 * rng.integers(1, max(u // 32, 1) + 1, 4) if v < o + u)
-    rows.update(int(v) for v in rng.integers(0, w["out_rows"], 16))
-    case, res = _run_prefill(harness, w, rows=rows, project_all=False)
-    assert_out(case.out_bits(), res, rows=rows)
+# oracle results of the full-size workloads, computed once for both tile heights
+_FULL = {}
+
+
+def _full_oracle(name):
+    if name not in _FULL:
+        w = workloads.build_named(name)
+        _FULL[name] = (w, O.compressor(w))
+    return _FULL[name]
+
+
+@pytest.mark.parametrize("name", ["varlen_c4a", "c4a_128k"])
+def test_full_size_every_row(harness, name, tile_rows):
+    """Every output row (windows and the exact +0 rows) and every state slot
+    of the full-size packed variable-length prefill (8 requests, 88826
+    tokens, H = 4096, resuming partial windows) and of the 128K-token C4A
+    prefill (H = 7168, Hadamard) against the oracle."""
+    _announce(f"{name} full size, every row, tile rows {tile_rows}")
+    w, res = _full_oracle(name)
+    case = harness.DeviceCase(w)
+    case.prefill()
+    torch.cuda.synchronize()
+    mx, mae = assert_out(case.out_bits(), res)
     kv, sc = case.states()
     assert_states(kv, sc, w, res)
     assert case.device_error() == 0
-
-
-def test_c4a_128k_sampled(harness, tile_rows):
-    _announce(f"c4a_128k full size, sampled rows, tile rows {tile_rows}")
-    w = workloads.build_named("c4a_128k")
-    rng = np.random.default_rng(6)
-    rows = ({0, 1, 2, 31, 32, 33, 63, 64, 32736, 32767}
-            | set(int(v) for v in rng.integers(0, 32768, 40)))
-    case, res = _run_prefill(harness, w, rows=rows, project_all=False)
-    mx, mae = assert_out(case.out_bits(), res, rows=rows)
-    kv, sc = case.states()
-    assert_states(kv, sc, w, res)
-    assert case.device_error() == 0
-    print(f"c4a_128k sampled: max scaled err {mx:.2e}, MAE {mae:.2e}")
+    nwin = len(res.window_rows)
+    print(f"{name} tile rows {tile_rows}: {nwin} windows of {w['out_rows']} rows, "
+          f"max scaled err {mx:.2e}, MAE {mae:.2e}")
+    del case
+    torch.cuda.empty_cache()
 
 
 # --------------------------------------------------------------------------

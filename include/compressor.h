@@ -215,6 +215,30 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* arg
  * errors are those of compressor_prefill. */
 int compressor_decode(const compressor_shape* shape, const compressor_args* args, void* stream);
 
+/* Bytes of the per-device scratch compressor_decode_noalloc uses in place of
+ * a workspace; every decode call the library accepts fits. */
+#define CMP_DECODE_SCRATCH_BYTES (12u << 20)
+
+/* compressor_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels, results and limits as
+ * compressor_decode, except that args->workspace and args->workspace_bytes
+ * are ignored: the call works in a scratch array of CMP_DECODE_SCRATCH_BYTES
+ * that the library holds on each device it runs on until the process ends.
+ * No call allocates or frees anything.  Every call on a device shares that
+ * device's scratch, so calls that overlap on one device (on different
+ * streams, or from different threads) race and must be ordered by the
+ * caller.  The scratch keeps the last call's contents; nothing in it is
+ * read before the call writes it.
+ * device_error  (device) uint32 word, may be NULL: the call ORs its
+ *               CMP_DEVERR_* bits into it (the caller clears it);
+ *               compressor_last_device_error does not apply to this entry
+ *               point.
+ * Returns the statuses of compressor_decode; CMP_ERR_WORKSPACE if the
+ * call's layout exceeded the scratch (no accepted shape does). */
+int compressor_decode_noalloc(const compressor_shape* shape, const compressor_args* args,
+                              uint32_t* device_error, void* stream);
+
 /* Quantised write of compressed rows into a paged FP8 cache, the step after
  * the operator that stores its rows into the Lightning Indexer / Sparse Flash
  * Attention compressed caches ([PyPTO] DeepSeek-V4 整网集成方式: those caches

@@ -26,7 +26,8 @@ EXPORTS = ("compressor_prefill_workspace_size", "compressor_decode_workspace_siz
            "compressor_pack_weights", "compressor_state_init", "compressor_state_reset",
            "compressor_prefill", "compressor_decode", "compressor_last_device_error",
            "compressor_status_str", "compressor_timing_enable", "compressor_timing_query",
-           "compressor_epilog", "compressor_set_prefill_tile_rows", "nsa_compress_with_cache")
+           "compressor_epilog", "compressor_set_prefill_tile_rows", "nsa_compress_with_cache",
+           "compressor_decode_noalloc")
 NSA_BF16, NSA_F16 = 0, 1
 NSA_LAYOUT_PAGED, NSA_LAYOUT_TND = 0, 1
 NSA_DEVERR_SLOT, NSA_DEVERR_TABLE, NSA_DEVERR_SEQLEN = 1, 2, 4
@@ -97,6 +98,7 @@ def library():
             "compressor_state_reset": (sp, vp, vp, vp, vp, vp, i32, i32, vp, vp),
             "compressor_prefill": (sp, ap, vp),
             "compressor_decode": (sp, ap, vp),
+            "compressor_decode_noalloc": (sp, ap, vp, vp),
             "compressor_last_device_error": (vp, vp, ctypes.POINTER(i32)),
             "compressor_timing_enable": (i32,),
             "compressor_set_prefill_tile_rows": (i32,),
@@ -197,7 +199,7 @@ def make_args(*, x, batch, kv_state, score_state, state_block_table, w_packed, a
               sin, cos, out, workspace, cu_seqlens=None, seqused=None, start_pos=None,
               kv_block_table=None, hadamard=None) -> Args:
     bf, f, i = torch.bfloat16, torch.float32, torch.int32
-    if workspace.dtype != torch.uint8:
+    if workspace is not None and workspace.dtype != torch.uint8:
         raise ValueError("workspace must be a uint8 tensor")
     return Args(
         x=_dev(x, bf, "x"), T=int(x.shape[0]), batch=int(batch),
@@ -210,7 +212,7 @@ def make_args(*, x, batch, kv_state, score_state, state_block_table, w_packed, a
         norm_weight=_dev(norm_weight, bf, "norm_weight"), hadamard=_dev(hadamard, bf, "hadamard"),
         sin=_dev(sin, bf, "sin"), cos=_dev(cos, bf, "cos"), out=_dev(out, bf, "out"),
         out_rows=int(out.shape[0]), workspace=_dev(workspace, torch.uint8, "workspace"),
-        workspace_bytes=int(workspace.numel()))
+        workspace_bytes=0 if workspace is None else int(workspace.numel()))
 
 
 def compressor_prefill(shape: Shape, args: Args, stream=None) -> None:
@@ -221,6 +223,16 @@ def compressor_prefill(shape: Shape, args: Args, stream=None) -> None:
 def compressor_decode(shape: Shape, args: Args, stream=None) -> None:
     _check("compressor_decode",
            library().compressor_decode(ctypes.byref(shape), ctypes.byref(args), _stream(stream)))
+
+
+def compressor_decode_noalloc(shape: Shape, args: Args, device_error: torch.Tensor = None,
+                              stream=None) -> None:
+    """compressor_decode in the library's per-device scratch: args.workspace
+    is ignored; device_error (int32 [1], optional) receives the call's
+    device error bits (the caller clears it)."""
+    _check("compressor_decode_noalloc", library().compressor_decode_noalloc(
+        ctypes.byref(shape), ctypes.byref(args), _dev(device_error, torch.int32, "device_error"),
+        _stream(stream)))
 
 
 def compressor_last_device_error(workspace: torch.Tensor, stream=None) -> int:

@@ -213,13 +213,13 @@ DecodeLayout decode_layout(const Cfg& cf, int B) {
   return L;
 }
 
-int check_args(const Cfg& cf, const compressor_args* a, bool decode) {
+int check_args(const Cfg& cf, const compressor_args* a, bool decode, bool own_workspace = true) {
   if (!a) return CMP_ERR_NULLPTR;
   if (a->batch < 1 || a->T < 0) return CMP_ERR_INVALID;
   if (a->out_rows < 0) return CMP_ERR_OUT_ROWS;
   if (a->T > 0 && !a->x) return CMP_ERR_NULLPTR;
   if (!a->kv_state || !a->score_state || !a->state_block_table || !a->w_packed || !a->ape ||
-      !a->norm_weight || !a->out || !a->workspace)
+      !a->norm_weight || !a->out || (own_workspace && !a->workspace))
     return CMP_ERR_NULLPTR;
   if (a->out_rows > 0 && (!a->sin || !a->cos)) return CMP_ERR_NULLPTR;
   if (cf.rotate && !a->hadamard) return CMP_ERR_NULLPTR;
@@ -260,7 +260,100 @@ int ensure_lds_limits() {
   return status == hipSuccess ? CMP_OK : CMP_ERR_HIP;
 }
 
+// One decode call on workspace ws (at least decode_layout(...).total bytes);
+// err2, if not NULL, also receives the tails' error bits.
+int decode_impl(Cfg cf, const DecodeLayout& L, const compressor_args* a, uint8_t* ws,
+                uint32_t* err2, hipStream_t st) {
+  uint32_t* err = reinterpret_cast<uint32_t*>(ws + L.err);
+  float* partial = reinterpret_cast<float*>(ws + L.partial);
+  float* pp = reinterpret_cast<float*>(ws + L.pp);
+  int32_t* ppflag = reinterpret_cast<int32_t*>(ws + L.ppflag);
+  DecRec* rec = reinterpret_cast<DecRec*>(ws + L.rec);
+  const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
+  const int B = a->batch;
+  const int T = a->T;
+  const uint16_t* cosv = static_cast<const uint16_t*>(a->cos);
+  const uint16_t* sinv = static_cast<const uint16_t*>(a->sin);
+  // the most windows a request can complete: its tokens (one without
+  // cu_seqlens, else at most 4 and at most T) span ceil(tokens / ratio)
+  const int max_tok = a->cu_seqlens ? std::min(T, DEC_MAX_TOK) : 1;
+  const int nwin = std::max(1, std::min(DEC_MAX_WIN, (max_tok + cf.ratio - 1) / cf.ratio));
+  const int side = B * nwin * L.split;
+  const int ks = decode_ksplit(cf, side);
+  const dim3 gg(side + cf.N / 32 * ks);
+  const int nrb = T <= 32 ? 1 : 2;
+  const int run = decode_run(cf, ks, nrb);
+  CMP_TRY(launch("decode_main", st, [&] {
+    const uint16_t* X = static_cast<const uint16_t*>(a->x);
+    const uint16_t* W = static_cast<const uint16_t*>(a->w_packed);
+    decltype(&decode_main_kernel<1, 8, 4, 2>) kern = nullptr;
+    with_ratio(cf.ratio, [&]<int R>() {
+      constexpr int C = coff_of<R>();
+      kern = nrb == 2 ? decode_main_kernel<2, 4, R, C>
+                      : (run == 8 ? decode_main_kernel<1, 8, R, C> : decode_main_kernel<1, 4, R, C>);
+    });
+    hipLaunchKernelGGL(kern, gg, dim3(GV_THREADS), 0, st, cf, X, W, partial, B, T, nwin, ks,
+                       a->cu_seqlens, a->seqused, a->start_pos, a->kv_state, a->score_state, kvt,
+                       a->state_block_table, pp, ppflag, rec, err);
+  }));
+  return launch("decode_tail", st, [&] {
+    const uint16_t* gamma = static_cast<const uint16_t*>(a->norm_weight);
+    const uint16_t* had = static_cast<const uint16_t*>(a->hadamard);
+    uint16_t* out = static_cast<uint16_t*>(a->out);
+    if (a->cu_seqlens) {
+      decltype(&decode_tail_kernel<4, 2, 8>) tail = nullptr;
+      with_ratio(cf.ratio, [&]<int R>() {
+        constexpr int C = coff_of<R>();
+        tail = ks <= 8 ? decode_tail_kernel<R, C, 8>
+                         : (ks <= 16 ? decode_tail_kernel<R, C, 16>
+                                       : decode_tail_kernel<R, C, DEC_MAX_KSPLIT>);
+      });
+      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, ks, B, T,
+                         a->cu_seqlens, a->seqused, a->start_pos, a->ape, a->kv_state,
+                         a->score_state, kvt, a->state_block_table, pp, ppflag, gamma, cosv,
+                         sinv, had, out, a->out_rows, err, err2);
+    } else {
+      // the tail loads a fixed number of K ranges (>= ks, <= DEC_MAX_KSPLIT)
+      decltype(&decode_tail1_kernel<4, 2, 8>) tail = nullptr;
+      with_ratio(cf.ratio, [&]<int R>() {
+        constexpr int C = coff_of<R>();
+        tail = ks <= 8 ? decode_tail1_kernel<R, C, 8>
+                         : (ks <= 16 ? decode_tail1_kernel<R, C, 16>
+                                       : decode_tail1_kernel<R, C, DEC_MAX_KSPLIT>);
+      });
+      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, ks, B, rec,
+                         a->ape, a->kv_state, a->score_state, pp, ppflag, gamma, cosv, sinv, had,
+                         out, a->out_rows, err, err2);
+    }
+  });
+}
+
 }  // namespace
+
+// Scratch of compressor_decode_noalloc: a fixed per-device array in place of
+// the caller's workspace.  Every decode workspace fits (decode calls are
+// bounded: batch <= 64, T <= 64; the largest layout, D = 512 at ratio 128
+// with H = 10240, needs under 12 MiB).  In host code the array's name is only
+// a stand-in for the symbol: its device address, taken per device with
+// hipGetSymbolAddress at the first call on that device, is what the kernels
+// get.
+static __device__ __align__(256) uint8_t scratch[CMP_DECODE_SCRATCH_BYTES];
+
+static int scratch_address(void** out) {
+  static std::mutex mu;
+  static std::vector<void*> ptrs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return CMP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CMP_ERR_HIP;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return CMP_OK;
+}
 
 extern "C" {
 
@@ -440,70 +533,21 @@ int compressor_decode(const compressor_shape* shape, const compressor_args* a, v
   CMP_TRY(check_args(cf, a, true));
   const DecodeLayout L = decode_layout(cf, a->batch);
   if (a->workspace_bytes < L.total) return CMP_ERR_WORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
-  uint32_t* err = reinterpret_cast<uint32_t*>(ws + L.err);
-  float* partial = reinterpret_cast<float*>(ws + L.partial);
-  float* pp = reinterpret_cast<float*>(ws + L.pp);
-  int32_t* ppflag = reinterpret_cast<int32_t*>(ws + L.ppflag);
-  DecRec* rec = reinterpret_cast<DecRec*>(ws + L.rec);
-  const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
-  const int B = a->batch;
-  const int T = a->T;
-  const uint16_t* cosv = static_cast<const uint16_t*>(a->cos);
-  const uint16_t* sinv = static_cast<const uint16_t*>(a->sin);
-  // the most windows a request can complete: its tokens (one without
-  // cu_seqlens, else at most 4 and at most T) span ceil(tokens / ratio)
-  const int max_tok = a->cu_seqlens ? std::min(T, DEC_MAX_TOK) : 1;
-  const int nwin = std::max(1, std::min(DEC_MAX_WIN, (max_tok + cf.ratio - 1) / cf.ratio));
-  const int side = B * nwin * L.split;
-  const int ks = decode_ksplit(cf, side);
-  const dim3 gg(side + cf.N / 32 * ks);
-  const int nrb = T <= 32 ? 1 : 2;
-  const int run = decode_run(cf, ks, nrb);
-  CMP_TRY(launch("decode_main", st, [&] {
-    const uint16_t* X = static_cast<const uint16_t*>(a->x);
-    const uint16_t* W = static_cast<const uint16_t*>(a->w_packed);
-    decltype(&decode_main_kernel<1, 8, 4, 2>) kern = nullptr;
-    with_ratio(cf.ratio, [&]<int R>() {
-      constexpr int C = coff_of<R>();
-      kern = nrb == 2 ? decode_main_kernel<2, 4, R, C>
-                      : (run == 8 ? decode_main_kernel<1, 8, R, C> : decode_main_kernel<1, 4, R, C>);
-    });
-    hipLaunchKernelGGL(kern, gg, dim3(GV_THREADS), 0, st, cf, X, W, partial, B, T, nwin, ks,
-                       a->cu_seqlens, a->seqused, a->start_pos, a->kv_state, a->score_state, kvt,
-                       a->state_block_table, pp, ppflag, rec, err);
-  }));
-  return launch("decode_tail", st, [&] {
-    const uint16_t* gamma = static_cast<const uint16_t*>(a->norm_weight);
-    const uint16_t* had = static_cast<const uint16_t*>(a->hadamard);
-    uint16_t* out = static_cast<uint16_t*>(a->out);
-    if (a->cu_seqlens) {
-      decltype(&decode_tail_kernel<4, 2, 8>) tail = nullptr;
-      with_ratio(cf.ratio, [&]<int R>() {
-        constexpr int C = coff_of<R>();
-        tail = ks <= 8 ? decode_tail_kernel<R, C, 8>
-                         : (ks <= 16 ? decode_tail_kernel<R, C, 16>
-                                       : decode_tail_kernel<R, C, DEC_MAX_KSPLIT>);
-      });
-      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, ks, B, T,
-                         a->cu_seqlens, a->seqused, a->start_pos, a->ape, a->kv_state,
-                         a->score_state, kvt, a->state_block_table, pp, ppflag, gamma, cosv,
-                         sinv, had, out, a->out_rows, err);
-    } else {
-      // the tail loads a fixed number of K ranges (>= ks, <= DEC_MAX_KSPLIT)
-      decltype(&decode_tail1_kernel<4, 2, 8>) tail = nullptr;
-      with_ratio(cf.ratio, [&]<int R>() {
-        constexpr int C = coff_of<R>();
-        tail = ks <= 8 ? decode_tail1_kernel<R, C, 8>
-                         : (ks <= 16 ? decode_tail1_kernel<R, C, 16>
-                                       : decode_tail1_kernel<R, C, DEC_MAX_KSPLIT>);
-      });
-      hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, ks, B, rec,
-                         a->ape, a->kv_state, a->score_state, pp, ppflag, gamma, cosv, sinv, had,
-                         out, a->out_rows, err);
-    }
-  });
+  return decode_impl(cf, L, a, static_cast<uint8_t*>(a->workspace), nullptr,
+                     static_cast<hipStream_t>(stream));
+}
+
+int compressor_decode_noalloc(const compressor_shape* shape, const compressor_args* a,
+                              uint32_t* device_error, void* stream) {
+  Cfg cf;
+  CMP_TRY(check_shape(shape, &cf));
+  CMP_TRY(check_args(cf, a, true, false));
+  const DecodeLayout L = decode_layout(cf, a->batch);
+  if (L.total > CMP_DECODE_SCRATCH_BYTES) return CMP_ERR_WORKSPACE;
+  void* ws = nullptr;
+  CMP_TRY(scratch_address(&ws));
+  return decode_impl(cf, L, a, static_cast<uint8_t*>(ws), device_error,
+                     static_cast<hipStream_t>(stream));
 }
 
 int compressor_last_device_error(const void* workspace, void* stream, int32_t* code) {

@@ -348,6 +348,13 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
 // ---------------------------------------------------------------------------
 constexpr int TL_THREADS = 512;
 
+// Error bits of the tails: into the call's error word, and into the caller's
+// word err2 as well when one is given (the allocation-free entry point)
+__device__ __forceinline__ void dec_report(uint32_t* err, uint32_t* err2, uint32_t bits) {
+  set_error(err, bits);
+  if (err2) set_error(err2, bits);
+}
+
 // kv and score (before Ape) of channel c of tokens t0 .. t0 + TC - 1 (packed
 // rows row0 + t, t < n), in every channel set: the K-range partials of the
 // TC tokens all in flight at once (KSB >= KS ranges each, unconditionally:
@@ -401,7 +408,7 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
     const float* __restrict__ pp, const int32_t* __restrict__ ppflag,
     const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ cosv,
     const uint16_t* __restrict__ sinv, const uint16_t* __restrict__ had, uint16_t* __restrict__ out,
-    int out_rows, uint32_t* __restrict__ err) {
+    int out_rows, uint32_t* __restrict__ err, uint32_t* __restrict__ err2) {
   constexpr int NSPLIT = dec_split<R>();
   __shared__ float red[TL_THREADS / 64];
   __shared__ float yv[512];
@@ -457,7 +464,7 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
   const int total = __shfl(incl, 63, 64);
 
   if ((int)blockIdx.x == B) {                    // rows after the last request's
-    if (total > out_rows && tid == 0) set_error(err, CMP_DEVERR_OUT_ROWS);
+    if (total > out_rows && tid == 0) dec_report(err, err2, CMP_DEVERR_OUT_ROWS);
     for (long i = (long)total * D + tid; i < (long)out_rows * D; i += TL_THREADS) out[i] = 0;
     return;
   }
@@ -468,12 +475,12 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
   q.n = __shfl(qj.n, b, 64);
   q.row0 = __shfl(qj.row0, b, 64);
   q.bad = (uint32_t)__shfl((int)qj.bad, b, 64);
-  if (q.bad && tid == 0) set_error(err, q.bad);
+  if (q.bad && tid == 0) dec_report(err, err2, q.bad);
   const int n = q.n, s = q.s, e = s + n;
   if (n == 0) return;
   const int ub = (n + R - 1) / R;
   if (o + ub > out_rows) {
-    if (tid == 0) set_error(err, CMP_DEVERR_OUT_ROWS);
+    if (tid == 0) dec_report(err, err2, CMP_DEVERR_OUT_ROWS);
     return;
   }
   const int w0 = s / R, nwin = e / R - w0;       // windows completed here (<= 2)
@@ -528,7 +535,7 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
     const int w = w0 + k;
     if (tid < NSPLIT) {
       const int32_t f = ppflag[(b * DEC_MAX_WIN + k) * NSPLIT + tid];
-      if (f) set_error(err, (uint32_t)f);
+      if (f) dec_report(err, err2, (uint32_t)f);
     }
     float pooled = 0.f;
     if (own) {
@@ -636,7 +643,7 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
       }
     }
   }
-  if (tbad && tid == 0) set_error(err, tbad);
+  if (tbad && tid == 0) dec_report(err, err2, tbad);
 }
 
 // Decode tail for one row per request (no cu_seqlens): the general tail
@@ -653,7 +660,7 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail1_kernel(
     const float* __restrict__ pp, const int32_t* __restrict__ ppflag,
     const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ cosv,
     const uint16_t* __restrict__ sinv, const uint16_t* __restrict__ had, uint16_t* __restrict__ out,
-    int out_rows, uint32_t* __restrict__ err) {
+    int out_rows, uint32_t* __restrict__ err, uint32_t* __restrict__ err2) {
   constexpr int NSPLIT = dec_split<R>();
   __shared__ float red[TL_THREADS / 64];
   __shared__ float yv[512];
@@ -663,7 +670,7 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail1_kernel(
   if ((int)blockIdx.x == B) {                    // rows after the last request's
     const DecRec t = rec[B];
     const int total = t.s;
-    if (tid == 0) set_error(err, (uint32_t)t.o | (total > out_rows ? CMP_DEVERR_OUT_ROWS : 0u));
+    if (tid == 0) dec_report(err, err2, (uint32_t)t.o | (total > out_rows ? CMP_DEVERR_OUT_ROWS : 0u));
     for (long i = (long)total * D + tid; i < (long)out_rows * D; i += TL_THREADS) out[i] = 0;
     return;
   }
@@ -720,7 +727,7 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail1_kernel(
   const bool completing = (rb.flags & DR_COMP) != 0;
   if (completing && tid < NSPLIT) {
     const int32_t f = ppflag[b * DEC_MAX_WIN * NSPLIT + tid];
-    if (f) set_error(err, (uint32_t)f);
+    if (f) dec_report(err, err2, (uint32_t)f);
   }
   // the rotary values of this channel for output row o
   const int rope0 = D - cf.rope;
@@ -799,7 +806,7 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail1_kernel(
         score_state[rb.rs * cD + cs * D + c] = zc[cs];
       }
     } else if (c == 0) {
-      set_error(err, CMP_DEVERR_TABLE);
+      dec_report(err, err2, CMP_DEVERR_TABLE);
     }
   }
 }

@@ -129,3 +129,23 @@ def test_epilog_argument_checks_before_any_launch():
         assert f(None, n, d, None, None, None, slots, None, None) == 2, (n, d, slots)
     # the block count must stay below 2^31
     assert f(None, 2 ** 31 - 1, 8192, None, None, None, 8, None, None) == 2
+
+
+def test_every_decode_layout_fits_the_noalloc_scratch():
+    """compressor_decode_noalloc works in a fixed per-device scratch of
+    CMP_DECODE_SCRATCH_BYTES: the decode workspace of every accepted shape
+    at the largest batch fits it."""
+    src = open(os.path.join(ROOT, "include", "compressor.h")).read()
+    m = re.search(r"#define CMP_DECODE_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    limit = int(m.group(1)) << int(m.group(2))
+    worst = 0
+    for r in (2, 4, 8, 16, 32, 64, 128):
+        for d in (128, 512):
+            for h in range(1024, 10241, 512):
+                coff = 2 if r == 4 else 1
+                sh = cmp.make_shape(r, d, h, False, 16, 64, -(-coff * r // 16))
+                worst = max(worst, cmp.compressor_decode_workspace_size(sh, 64, 64))
+    assert 0 < worst <= limit, (worst, limit)
+    lib = cmp.library()
+    sh = cmp.make_shape(4, 512, 4096, False, 256, 8, 1)
+    assert lib.compressor_decode_noalloc(ctypes.byref(sh), None, None, None) == 1

@@ -81,8 +81,11 @@ def bench_prefill(steps, warmup, name="c4a_128k"):
             kernels[k] = ms / n
     cmp.compressor_timing_enable(False)
     windows = w["T"] // w["ratio"]
+    out_bits = case.out_bits().copy()
+    kv, sc = case.states()
     return dict(w=w, ms_per_step=total_ms / steps, windows=windows, kernels=kernels,
-                device=torch.cuda.get_device_name(0))
+                device=torch.cuda.get_device_name(0), out_bits=out_bits, kv=kv.copy(),
+                sc=sc.copy())
 
 
 def decode_bytes(w):
@@ -274,16 +277,29 @@ def bench_nsa(steps, copies=9):
             "config": "128 sequences, 32 heads x 128, window 32, stride 16, page 128, bf16"}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s=20.0):
     """The oracle, untuned, on a bounded sample of the 128K workload: whole
     windows (projection of their rows, pooling, RMSNorm, RoPE, Hadamard),
-    as many as fit the time budget (at most every window of the workload)."""
+    as many as fit the time budget (at most every window of the workload).
+    Returns the baseline record and the oracle result with its window rows
+    (for the parity statistics of the timed call)."""
     from oracle import compressor_oracle as O
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        blas = None
+    cores = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(0)
 
     def run(n):
@@ -298,14 +314,49 @@ def cpu_baseline(w, budget_s=20.0):
     per = max((tb - ta) / (nb - na), 1e-6)
     fixed = max(ta - na * per, 0.0)
     n2 = int(max(nb, min(w["out_rows"], (budget_s - fixed) / per)))
+    rows = rng.choice(w["out_rows"], n2, replace=False)
     t0 = time.perf_counter()
-    O.compressor(w, windows=rng.choice(w["out_rows"], n2, replace=False), project_all=False)
+    res = O.compressor(w, windows=rows, project_all=False)
     dt2 = time.perf_counter() - t0
-    return {"value": n2 / dt2, "unit": "compressed tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{n2} random windows of the 128K C4A workload (their 8 projected rows "
-                      f"each, pooling, RMSNorm, RoPE, Hadamard) plus the state rows, fp64 numpy, "
-                      f"{dt2:.1f} s"}
+    rec = {"value": n2 / dt2, "unit": "compressed tokens/s", "cores": cores,
+           "blas_threads": blas, "cpu_model": cpu_model(), "kind": "oracle",
+           "sample": f"{n2} random windows of the 128K C4A workload (their 8 projected rows "
+                     f"each, pooling, RMSNorm, RoPE, Hadamard) plus the state rows, fp64 numpy, "
+                     f"{dt2:.1f} s"}
+    return rec, res, rows
+
+
+def parity_stats(pre, res, rows):
+    """The timed call's output rows and state against the oracle, on the rows
+    the CPU baseline computed: max scaled error |g - o| / max(|o|, rms(row)),
+    mean absolute error, the exact +0 rows, the largest state error
+    |g - o| / max(|o|, 1) and the written-slot mask mismatches."""
+    from oracle import compressor_oracle as O
+    w = pre["w"]
+    done = np.zeros(w["out_rows"], bool)
+    for _, _, row in res.window_rows:
+        done[row] = True
+    rows = np.sort(np.asarray(rows))
+    win = rows[done[rows]]
+    zero = rows[~done[rows]]
+    g = O.bf16_to_f64(pre["out_bits"][win])
+    o = res.out[win]
+    rms = np.sqrt(np.mean(o * o, axis=1, keepdims=True))
+    scaled = np.abs(g - o) / np.maximum(np.abs(o), rms)
+    st_err, mism = 0.0, 0
+    for gp, inp, ref, wr in ((pre["kv"], w["kv_state"], res.kv_state, res.kv_written),
+                             (pre["sc"], w["score_state"], res.score_state, res.score_written)):
+        changed = np.any(gp.view(np.uint32) != np.asarray(inp, np.float32).view(np.uint32), axis=2)
+        mism += int(np.sum(changed != wr))
+        if wr.any():
+            e = np.abs(gp[wr].astype(np.float64) - ref[wr]) / np.maximum(np.abs(ref[wr]), 1.0)
+            st_err = max(st_err, float(e.max()))
+    return {"rows_checked": int(rows.size), "window_rows": int(win.size),
+            "max_scaled_err": float(scaled.max()) if win.size else 0.0,
+            "mae": float(np.mean(np.abs(g - o))) if win.size else 0.0,
+            "zero_rows_nonzero": int(np.sum(np.any(pre["out_bits"][zero] != 0, axis=1))),
+            "state_max_err": st_err, "written_mask_mismatches": mism,
+            "tolerances": {"out": 2e-2, "state": 1e-3}}
 
 
 # ---------------------------------------------------------------------------
@@ -319,6 +370,15 @@ PROFILE_COMMANDS = {
              "python3 bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline",
     "write": "rocprofv3 --pmc WRITE_SIZE -T --output-format csv -d {out}/write -o run -- "
              "python3 bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline",
+    "dkt": "rocprofv3 --kernel-trace --stats -T --output-format csv -d {out}/dkt -o run -- "
+           "python3 bench.py --decode-only --decode-workloads decode_c4a,decode_c128a "
+           "--decode-steps 100",
+    "dfetch": "rocprofv3 --pmc FETCH_SIZE -T --output-format csv -d {out}/dfetch -o run -- "
+              "python3 bench.py --decode-only --decode-workloads decode_c4a,decode_c128a "
+              "--decode-steps 24",
+    "dwrite": "rocprofv3 --pmc WRITE_SIZE -T --output-format csv -d {out}/dwrite -o run -- "
+              "python3 bench.py --decode-only --decode-workloads decode_c4a,decode_c128a "
+              "--decode-steps 24",
     "cfetch": "rocprofv3 --pmc FETCH_SIZE -T --output-format csv -d {out}/cfetch -o run -- "
               "python3 bench.py --copy-calibration",
     "cwrite": "rocprofv3 --pmc WRITE_SIZE -T --output-format csv -d {out}/cwrite -o run -- "
@@ -371,18 +431,19 @@ def summarize_profiles(out):
              if GEMM_KERNEL in r["Kernel_Name"]]
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
-    # the command's 128K C4A launches come first: 15 warm-up, 20 timed and 10
-    # in the per-kernel event pass; the other prefill workloads follow
+    # the other prefill workloads run first (each 5 warm-up + 10 timed + 10 in
+    # the event pass); the command's 128K C4A launches come last: 15 warm-up,
+    # 20 timed and 10 in the per-kernel event pass
     n_head = 15 + 20 + 10
     if len(dur) >= n_head:
-        head, rest = dur[:n_head], dur[n_head:]
+        rest, head = dur[:-n_head], dur[-n_head:]
         lines += ["", f"`{GEMM_KERNEL}` per launch of the 128K C4A prefill (ms, from the kernel "
                   "trace, in launch order): " + ", ".join(f"{x:.3f}" for x in head) + ".",
                   f"Average after the 15 warm-up launches: {np.mean(head[15:]):.3f} ms; average "
                   f"of its last 10 (the per-kernel event pass that bench.py's roofline times): "
                   f"{np.mean(head[-10:]):.3f} ms."]
         if rest:
-            lines += ["", "Later launches (the 8192-token C128A prefill, then the packed "
+            lines += ["", "Earlier launches (the 8192-token C128A prefill, then the packed "
                       "variable-length C4A prefill, each warm-up + timed + event pass; ms): "
                       + ", ".join(f"{x:.3f}" for x in rest) + "."]
     lines += ["", f"Kernel source hash (gemm.hpp + pool.hpp + common.hpp): `{sha}`."]
@@ -415,8 +476,80 @@ def summarize_profiles(out):
     }
     json.dump(doc, open(os.path.join(ROOT, "profiles", "gemm_c4a_128k_traffic.json"), "w"),
               indent=1)
+    if os.path.isdir(os.path.join(out, "dkt")):
+        summarize_decode(out, fscale, wscale)
     print(json.dumps({"kernel_stats_rows": len(rows), "hbm_bytes_per_launch": fb + wb,
                       "sha": sha}))
+
+
+def summarize_decode(out, fscale, wscale):
+    """profiles/decode_kernels.md: per-kernel durations of the decode step
+    (32 requests, C4A and C128A, H = 7168) from the dkt trace, and HBM bytes
+    per dispatch of decode_main_kernel from the dfetch / dwrite counter runs,
+    scaled by the copy calibration, against the algorithmic bytes."""
+    import csv
+    import workloads
+    sha = kernel_source_sha("decode.hpp", "common.hpp")
+    trace = list(csv.DictReader(open(_find_csv(os.path.join(out, "dkt"), "kernel_trace.csv"))))
+    # the runs time decode_c4a, then decode_c128a, with the same step counts:
+    # the first half of each kernel's launches (in dispatch order) belongs to
+    # decode_c4a, the second half to decode_c128a
+    order = ("decode_c4a", "decode_c128a")
+
+    def halves(rows, key):
+        rows = sorted(rows, key=lambda r: int(r[key]))
+        h = len(rows) // 2
+        return {order[0]: rows[:h], order[1]: rows[h:]}
+
+    lines = ["# Decode kernels: 32-request step, H = 7168, D = 512", "",
+             "Commands (from the repository root, on one MI355X):", "", "```"]
+    lines += [PROFILE_COMMANDS[k].format(out="gpurun_out") for k in ("dkt", "dfetch", "dwrite",
+                                                                    "cfetch", "cwrite")]
+    lines += ["```", "",
+              "Durations from the kernel trace (every launch of the run: eager, graph-replayed "
+              "and event-timed steps; the panel, x and pools rotate over 12 copies, beyond the "
+              "256 MB last-level cache).  Bytes per dispatch: FETCH_SIZE and WRITE_SIZE "
+              f"(KiB) times the copy calibration (x{fscale:.3f} and x{wscale:.3f}), median over "
+              "the dispatches of the counter runs.", "",
+              "| workload | kernel | launches | median us | p10 us | p90 us | fetch MB | "
+              "write MB | algorithmic MB | fetch / median time |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    counters = {}
+    for folder, counter in (("dfetch", "FETCH_SIZE"), ("dwrite", "WRITE_SIZE")):
+        rows = [r for r in csv.DictReader(open(_find_csv(os.path.join(out, folder),
+                                                         "counter_collection.csv")))
+                if r["Counter_Name"] == counter]
+        for kind in ("main", "tail"):
+            sel = [r for r in rows if "decode_" + kind in r["Kernel_Name"]]
+            for wl, part in halves(sel, "Dispatch_Id").items():
+                counters[(wl, kind, counter)] = [float(r["Counter_Value"]) for r in part]
+    for wl in order:
+        w = workloads.build_named(wl, with_x=False)
+        w["x"] = np.zeros((w["T"], w["hidden"]), np.uint16)
+        alg = decode_bytes(w) / 1e6
+        for kind in ("main", "tail"):
+            sel = [r for r in trace if "decode_" + kind in r["Kernel_Name"]]
+            part = halves(sel, "Start_Timestamp")[wl]
+            d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in part]
+            f = counters.get((wl, kind, "FETCH_SIZE"), [])
+            wv = counters.get((wl, kind, "WRITE_SIZE"), [])
+            fb = float(np.median(f)) * 1024 * fscale / 1e6 if f else float("nan")
+            wb = float(np.median(wv)) * 1024 * wscale / 1e6 if wv else float("nan")
+            med = float(np.median(d))
+            alg_s = f"{alg:.2f}" if kind == "main" else "-"
+            lines.append(f"| {wl} | decode_{kind} | {len(d)} | {med:.2f} | "
+                         f"{np.percentile(d, 10):.2f} | {np.percentile(d, 90):.2f} | {fb:.2f} | "
+                         f"{wb:.2f} | {alg_s} | {fb / med:.2f} TB/s |")
+    lines += ["", "The algorithmic bytes of a step (panel, x, ring rows read, state rows and "
+              "output rows written) are all charged to decode_main in the table.",
+              f"Kernel source hash (decode.hpp + common.hpp): `{sha}`."]
+    open(os.path.join(ROOT, "profiles", "decode_kernels.md"), "w").write("\n".join(lines) + "\n")
+
+
+def progress(msg):
+    """One progress line per finished section, on stderr (stdout carries only
+    the JSON result)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -431,6 +564,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode workloads (for profiling runs)")
+    ap.add_argument("--decode-workloads", default=",".join(DECODE_WORKLOADS),
+                    help="comma-separated decode workloads for --decode-only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (scales HBM byte counters)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -456,11 +591,50 @@ def main():
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
         return
     if a.decode_only:
-        for name in DECODE_WORKLOADS:
+        names = [n for n in a.decode_workloads.split(",") if n]
+        for name in names:
             print(name, json.dumps(bench_decode(name, a.decode_steps, 5)), flush=True)
-        print("epilog_fp8", json.dumps(bench_epilog(a.decode_steps)), flush=True)
+        if set(names) == set(DECODE_WORKLOADS):
+            print("epilog_fp8", json.dumps(bench_epilog(a.decode_steps)), flush=True)
         return
+    extra = {}
+    if not a.no_decode:
+        # the secondary workloads first (their numbers are reported beside
+        # the headline); then the headline prefill's warm-up and timed steps
+        dec = {}
+        for name in DECODE_WORKLOADS:
+            d = bench_decode(name, a.decode_steps, 20)
+            progress(f"{name}: {d['us_per_step']:.2f} us per step")
+            dec[name] = {"us_per_step": d["us_per_step"],
+                         "us_per_step_eager": d["us_per_step_eager"],
+                         "launch_us_event_bracketed": d["kernels_us"],
+                         "algorithmic_bytes": d["step_bytes"],
+                         "hbm_frac": d["step_bytes"] / (d["us_per_step"] * 1e-6) / 1e9
+                         / PEAK_HBM_GBS}
+        extra["decode"] = dec
+        extra["decode_note"] = ("us_per_step: device time per step from HIP-graph replays; "
+                                "launch_us_event_bracketed: each launch between two HIP events "
+                                "in eager mode (event and launch overhead included, so the two "
+                                "add up to more than a step); kernel durations are in the "
+                                "rocprofv3 summaries under profiles/")
+        extra["nsa_compress"] = bench_nsa(a.decode_steps)
+        extra["epilog_fp8"] = bench_epilog(a.decode_steps)
+        progress("nsa and epilog done")
+        # the other prefill workloads: the 8192-token C128A call and the
+        # packed variable-length C4A continuation (8 requests, 88826 tokens)
+        other = {}
+        for name in ("c128a_8192", "varlen_c4a"):
+            p = bench_prefill(10, 5, name)
+            progress(f"{name}: {p['ms_per_step']:.3f} ms per call")
+            pw = p["w"]
+            fl = 2.0 * pw["T"] * pw["hidden"] * 2 * pw["coff"] * pw["head_dim"]
+            other[name] = {"ms_per_step": p["ms_per_step"], "kernels_ms": p["kernels"],
+                           "gemm_tflops": fl / (p["kernels"]["gemm"] * 1e-3) / 1e12,
+                           "gemm_mfma_frac": fl / (p["kernels"]["gemm"] * 1e-3) / 1e12
+                           / PEAK_BF16_TFLOPS, "tokens": pw["T"]}
+        extra["prefill_other"] = other
     pre = bench_prefill(a.steps, a.warmup)
+    progress(f"c4a_128k: {pre['ms_per_step']:.3f} ms per call")
     w = pre["w"]
     T, H, N = w["T"], w["hidden"], 2 * w["coff"] * w["head_dim"]
     gemm_ms = pre["kernels"]["gemm"]
@@ -483,37 +657,18 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm_pool_kernel",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": gemm_ms},
+                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": gemm_ms,
+                     "whole_call_frac": flops / (pre["ms_per_step"] * 1e-3) / 1e12
+                     / PEAK_BF16_TFLOPS},
         "kernels_ms": pre["kernels"],
         "device": pre["device"],
     }
-    if not a.no_decode:
-        dec = {}
-        for name in DECODE_WORKLOADS:
-            d = bench_decode(name, a.decode_steps, 20)
-            dec[name] = {"us_per_step": d["us_per_step"],
-                         "us_per_step_eager": d["us_per_step_eager"],
-                         "kernels_us": d["kernels_us"],
-                         "algorithmic_bytes": d["step_bytes"],
-                         "hbm_frac": d["step_bytes"] / (d["us_per_step"] * 1e-6) / 1e9
-                         / PEAK_HBM_GBS}
-        result["decode"] = dec
-        result["nsa_compress"] = bench_nsa(a.decode_steps)
-        result["epilog_fp8"] = bench_epilog(a.decode_steps)
-        # the other prefill workloads: the 8192-token C128A call and the
-        # packed variable-length C4A continuation (8 requests, 88826 tokens)
-        other = {}
-        for name in ("c128a_8192", "varlen_c4a"):
-            p = bench_prefill(10, 5, name)
-            pw = p["w"]
-            fl = 2.0 * pw["T"] * pw["hidden"] * 2 * pw["coff"] * pw["head_dim"]
-            other[name] = {"ms_per_step": p["ms_per_step"], "kernels_ms": p["kernels"],
-                           "gemm_tflops": fl / (p["kernels"]["gemm"] * 1e-3) / 1e12,
-                           "gemm_mfma_frac": fl / (p["kernels"]["gemm"] * 1e-3) / 1e12
-                           / PEAK_BF16_TFLOPS, "tokens": pw["T"]}
-        result["prefill_other"] = other
+    result.update(extra)
     if not a.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w)
+        base, res, rows = cpu_baseline(w)
+        result["cpu_baseline"] = base
+        result["parity"] = parity_stats(pre, res, rows)
+        progress("cpu baseline and parity done")
     print(json.dumps(result), flush=True)
 
 

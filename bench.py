@@ -75,7 +75,7 @@ def bench_prefill(steps, warmup, name="c4a_128k"):
         case.prefill()
     torch.cuda.synchronize()
     kernels = {}
-    for k in ("plan", "hadamard_pack", "prefix", "gemm", "post"):
+    for k in ("setup", "gemm", "post"):
         n, ms = cmp.compressor_timing_query(k)
         if n:
             kernels[k] = ms / n

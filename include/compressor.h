@@ -291,8 +291,9 @@ int compressor_set_prefill_tile_rows(int32_t rows);
 
 /* Kernel timing: while enabled, every kernel the library enqueues is
  * bracketed by a pair of HIP events on the same stream.  Enabling clears the
- * records.  Kernel names: "plan", "hadamard_pack", "prefix", "gemm" (projection
- * with the window pooling and state stores in its epilogue), "post",
+ * records.  Kernel names: "setup" (request plan, Hadamard check and packing,
+ * staging of earlier positions' ring rows), "gemm" (projection with the window
+ * pooling and state stores in its epilogue), "post",
  * "decode_main" (GEMV and ring pre-pooling),
  * "decode_tail", "pack", "state_fill", "epilog". */
 int compressor_timing_enable(int32_t on);

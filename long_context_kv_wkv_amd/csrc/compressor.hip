@@ -144,6 +144,10 @@ int device_cu_count() {
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// workgroups that check and pack the D x D Hadamard matrix (256 lane pieces
+// of 8 values each): 128 for D = 512, 8 for D = 128
+inline int hadamard_pack_wgs(const Cfg& cf) { return cf.rotate ? cf.D * cf.D / 8 / 256 : 0; }
+
 struct PrefillLayout {
   size_t err, tiles, hadflag, plan, pooled, hadF, staging, split, total;
 };
@@ -152,8 +156,9 @@ PrefillLayout prefill_layout(const Cfg& cf, int T, int B, int out_rows) {
   PrefillLayout L;
   size_t o = 0;
   L.err = 0;
-  L.tiles = 4;                             // error word, GEMM tile count, and
-  L.hadflag = 8;  o += 256;                // "Had is not a scaled Sylvester matrix"
+  L.tiles = 4;    o += 256;                // error word, GEMM tile count
+  // one "Had is not a scaled Sylvester matrix" flag per packing workgroup
+  L.hadflag = o;  o = align256(o + (size_t)hadamard_pack_wgs(cf) * 4);
   L.plan = o;     o = align256(o + (size_t)B * PL_WIDTH * 4);
   L.pooled = o;   o = align256(o + (size_t)out_rows * cf.D * 4);
   L.hadF = o;     o = align256(o + (cf.rotate ? (size_t)cf.D * cf.D * 2 : 0));
@@ -455,7 +460,7 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + L.err);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
-  uint32_t* had_general = reinterpret_cast<uint32_t*>(ws + L.hadflag);
+  uint32_t* had_flags = reinterpret_cast<uint32_t*>(ws + L.hadflag);
   int32_t* plan = reinterpret_cast<int32_t*>(ws + L.plan);
   float* pooled = reinterpret_cast<float*>(ws + L.pooled);
   uint16_t* hadF = reinterpret_cast<uint16_t*>(ws + L.hadF);
@@ -470,23 +475,15 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
   const int forced = g_tile_rows.load(std::memory_order_relaxed);
   cf.bm = forced ? forced : (long)((T + 255) / 256) * tiles_n < cus ? 128 : 256;
 
-  CMP_TRY(launch("plan", st, [&] {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, a->cu_seqlens,
-                       a->seqused, a->start_pos, B, T, cf.ratio, cf.coff, cf.bm, a->out_rows,
-                       plan, tiles, err, had_general);
+  const int nhad = hadamard_pack_wgs(cf);
+  const int nstage = T > 0 ? B * cf.coff * cf.ratio : 0;
+  CMP_TRY(launch("setup", st, [&] {
+    hipLaunchKernelGGL(setup_kernel, dim3(1 + nhad + nstage), dim3(SETUP_THREADS), 0, st, cf,
+                       a->cu_seqlens, a->seqused, a->start_pos, B, T, a->out_rows, plan, tiles,
+                       err, static_cast<const uint16_t*>(a->hadamard), hadF, had_flags, nhad,
+                       a->kv_state, a->score_state, kvt, a->state_block_table, staging);
   }));
-  if (cf.rotate) {
-    CMP_TRY(launch("hadamard_pack", st, [&] {
-      hipLaunchKernelGGL(hadamard_pack_kernel, dim3(cf.D * cf.D / 8 / 256), dim3(256), 0, st,
-                         static_cast<const uint16_t*>(a->hadamard), hadF, cf.D, had_general);
-    }));
-  }
   if (T > 0) {
-    CMP_TRY(launch("prefix", st, [&] {
-      hipLaunchKernelGGL(prefix_kernel, dim3(cf.coff * cf.ratio, B), dim3(256), 0, st, cf,
-                         a->kv_state, a->score_state, kvt, a->state_block_table, plan, staging,
-                         err);
-    }));
     // persistent: one workgroup per CU (a multiple of 8, one run of tiles
     // per XCD), never more than there are tiles
     const long nwg = (long)prefill_max_tiles(T, B, cf.bm) * tiles_n;
@@ -514,13 +511,13 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
         hipLaunchKernelGGL(post_kernel<8>, qg, dim3(256), lds, st, cf, pooled, split, plan, B,
                            a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
                            static_cast<const uint16_t*>(a->cos),
-                           static_cast<const uint16_t*>(a->sin), hadF, had_general,
+                           static_cast<const uint16_t*>(a->sin), hadF, had_flags, nhad,
                            static_cast<uint16_t*>(a->out));
       else
         hipLaunchKernelGGL(post_kernel<2>, qg, dim3(256), lds, st, cf, pooled, split, plan, B,
                            a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
                            static_cast<const uint16_t*>(a->cos),
-                           static_cast<const uint16_t*>(a->sin), hadF, had_general,
+                           static_cast<const uint16_t*>(a->sin), hadF, had_flags, nhad,
                            static_cast<uint16_t*>(a->out));
     }));
   }

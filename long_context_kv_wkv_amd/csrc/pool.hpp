@@ -3,7 +3,7 @@
 // Tiles are window-aligned per request.  A tile covers BM (256, or 128 for
 // short calls) consecutive positions P0 .. P0+BM-1 of one request (rows of x
 // where the position is a token of this call; earlier positions come from
-// the state ring, staged by prefix_kernel before the GEMM): 64 (32) windows
+// the state ring, staged by the setup launch before the GEMM): 64 (32) windows
 // for ratio 4, two (one) for ratio 128.
 // For ratio 4 (coff = 2) window w pools the first channel set of window w-1
 // and the second set of window w ([PyPTO] 压缩窗口与状态更新; [AscendC] C4A
@@ -82,32 +82,6 @@ __device__ __forceinline__ float soft_value2(Soft a, Soft b) {
   const float sb = b.l > 0.f ? __builtin_amdgcn_exp2f((b.m - mn) * kLog2e) : 0.f;
   const float den = a.l * sa + b.l * sb;
   return den > 0.f ? (a.x * sa + b.x * sb) / den : 0.f;
-}
-
-// Staging of the ring rows of positions [L_b, s_b) (positions >= 0): for
-// request b, row j = p - L_b holds the kv row (coff*D) then the score row.
-__global__ __launch_bounds__(256) void prefix_kernel(Cfg cf, const float* __restrict__ kv_state,
-                                                    const float* __restrict__ score_state,
-                                                    const int32_t* __restrict__ kv_tab,
-                                                    const int32_t* __restrict__ st_tab,
-                                                    const int32_t* __restrict__ plan,
-                                                    float* __restrict__ staging,
-                                                    uint32_t* __restrict__ err) {
-  const int b = blockIdx.y, j = blockIdx.x;
-  const int32_t* rec = plan + (long)b * PL_WIDTH;
-  const int p = rec[PL_FIRST] + j;
-  if (rec[PL_NTOK] == 0 || p < 0 || p >= rec[PL_START]) return;
-  const int cD = cf.coff * cf.D;
-  long rk, rs;
-  if (!state_row(cf, kv_tab, b, p, &rk) || !state_row(cf, st_tab, b, p, &rs)) {
-    if (threadIdx.x == 0) set_error(err, CMP_DEVERR_TABLE);
-    return;
-  }
-  float* dst = staging + ((size_t)b * cf.coff * cf.ratio + j) * 2 * cD;
-  for (int i = threadIdx.x; i < cD; i += blockDim.x) {
-    dst[i] = kv_state[rk * cD + i];
-    dst[cD + i] = score_state[rs * cD + i];
-  }
 }
 
 // Request whose tile range holds global M-tile `mt` (largest b with tile0 <= mt).
@@ -390,6 +364,15 @@ __device__ __forceinline__ void pool_epilogue(
   const int o = rec[PL_OUT0];
   const int live_lo = max(s, R * (e / R) - (COFF - 1) * R);   // state rows to store
   uint32_t bad = 0;
+  // the table entries of the staged rows (positions [max(first, 0), s)),
+  // which the staging skipped if out of range: checked once per request
+  if (tloc == 0 && tl.nt == 0 && wave == 0) {
+    for (int p = max(rec[PL_FIRST], 0) + lane; p < s; p += 64) {
+      long rk, rs;
+      if (!state_row(cf, kv_tab, b, p, &rk) || !state_row(cf, st_tab, b, p, &rs))
+        bad |= CMP_DEVERR_TABLE;
+    }
+  }
 
   if constexpr (COFF == 2) {
     // ---- ratio 4: lane (wn, lrow) owns channel c in all four variants ----

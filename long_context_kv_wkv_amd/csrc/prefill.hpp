@@ -6,9 +6,55 @@
 namespace cmp {
 
 // ---------------------------------------------------------------------------
+// Setup of a prefill call: one launch of three independent parts.
+//  * workgroup 0 plans the call (per-request start, length, windows, output
+//    rows and GEMM tiles) and writes the call's error word;
+//  * the next D*D/2048 workgroups (rotate only) check the Hadamard matrix
+//    and copy it to the MFMA fragment order;
+//  * the rest stage the ring rows of positions before each request's first
+//    token (read once here, before the GEMM stores any state row).
+// No part reads another's output, so they need no ordering inside the
+// launch; every later kernel of the call sees all three.
+// ---------------------------------------------------------------------------
+constexpr int SETUP_THREADS = 256;
+
+// Request b of a call, from cu_seqlens / seqused / start_pos, with the
+// argument checks of the plan (the planning workgroup and the staging
+// workgroups decode a request the same way):
+//   n_b = seqused[b] (or the slot length), s_b = start_pos[b] (or 0);
+//   an inconsistent slot, n or s makes the request empty and sets a bit.
+struct PReq {
+  int s, n, row0;
+  uint32_t bad;
+};
+__device__ __forceinline__ PReq prefill_request(int b, int B, int T,
+                                                const int32_t* __restrict__ cu_seqlens,
+                                                const int32_t* __restrict__ seqused,
+                                                const int32_t* __restrict__ start_pos) {
+  PReq q{0, 0, 0, 0u};
+  int c0, c1;
+  if (cu_seqlens) { c0 = cu_seqlens[b]; c1 = cu_seqlens[b + 1]; }
+  else { const int S = T / B; c0 = b * S; c1 = c0 + S; }
+  if (c0 < 0 || c1 < c0 || c1 > T) { q.bad |= CMP_DEVERR_SEQLEN; c0 = 0; c1 = 0; }
+  const int slot = c1 - c0;
+  int n = seqused ? seqused[b] : slot;
+  if (n < 0 || n > slot) { q.bad |= CMP_DEVERR_SEQLEN; n = n < 0 ? 0 : slot; }
+  int s = start_pos ? start_pos[b] : 0;
+  if (s < 0 || s > 0x7fffffff - n) { q.bad |= CMP_DEVERR_START_POS; s = 0; n = 0; }
+  q.s = s;
+  q.n = n;
+  q.row0 = c0;
+  return q;
+}
+
+// First position the GEMM tiles of a request starting at s cover (window
+// aligned, one window earlier for ratio 4: the halo of staged rows)
+__device__ __forceinline__ int prefill_first(int s, int ratio, int coff) {
+  return ratio * (s / ratio) - (coff - 1) * ratio;
+}
+
 // Plan: per-request start / length / windows / output rows, computed on the
-// device from cu_seqlens, seqused and start_pos (no host synchronisation).
-// Also clears the error word of this call.
+// device (no host synchronisation); also writes this call's error word.
 //   n_b   = seqused[b] (or the slot length)        e_b = s_b + n_b
 //   c_b   = floor(e_b / r) - floor(s_b / r)        windows completed here
 //   u_b   = ceil(n_b / r)                          output rows owned
@@ -16,17 +62,14 @@ namespace cmp {
 // Windows complete when (start_pos + i + 1) % ratio == 0 ([PyPTO]
 // 数值精度与验证要点), which is what c_b counts.  Rows per request and their
 // placement are the output layout documented in compressor.h.
-// One workgroup of 1024 threads; B is walked in chunks with a carried offset.
-// ---------------------------------------------------------------------------
-constexpr int PLAN_THREADS = 1024;
-
-__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
+// One workgroup; B is walked in chunks of SETUP_THREADS with a carried offset.
+__device__ __forceinline__ void plan_block(
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ seqused,
     const int32_t* __restrict__ start_pos, int B, int T, int ratio, int coff, int tile_rows,
     int out_rows, int32_t* __restrict__ plan, int32_t* __restrict__ tile_count,
-    uint32_t* __restrict__ err, uint32_t* __restrict__ had_general) {
-  __shared__ int scan[PLAN_THREADS];
-  __shared__ int scan2[PLAN_THREADS];
+    uint32_t* __restrict__ err) {
+  __shared__ int scan[SETUP_THREADS];
+  __shared__ int scan2[SETUP_THREADS];
   __shared__ uint32_t s_err;
   __shared__ int s_carry, s_tcarry;
   const int tid = threadIdx.x;
@@ -34,31 +77,22 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
   if (tid == 0) { s_err = 0; s_carry = 0; s_tcarry = 0; }
   __syncthreads();
   uint32_t my_err = 0;
-  for (int base = 0; base < B; base += PLAN_THREADS) {
+  for (int base = 0; base < B; base += SETUP_THREADS) {
     const int b = base + tid;
-    int s = 0, n = 0, row0 = 0;
-    if (b < B) {
-      int c0, c1;
-      if (cu_seqlens) { c0 = cu_seqlens[b]; c1 = cu_seqlens[b + 1]; }
-      else { const int S = T / B; c0 = b * S; c1 = c0 + S; }
-      if (c0 < 0 || c1 < c0 || c1 > T) { my_err |= CMP_DEVERR_SEQLEN; c0 = 0; c1 = 0; }
-      const int slot = c1 - c0;
-      n = seqused ? seqused[b] : slot;
-      if (n < 0 || n > slot) { my_err |= CMP_DEVERR_SEQLEN; n = n < 0 ? 0 : slot; }
-      s = start_pos ? start_pos[b] : 0;
-      if (s < 0 || s > 0x7fffffff - n) { my_err |= CMP_DEVERR_START_POS; s = 0; n = 0; }
-      row0 = c0;
-    }
+    PReq q{0, 0, 0, 0u};
+    if (b < B) q = prefill_request(b, B, T, cu_seqlens, seqused, start_pos);
+    my_err |= q.bad;
+    const int s = q.s, n = q.n;
     const int u = (n + ratio - 1) / ratio;
     // GEMM tiles: tile_rows positions each from the window start r*floor(s/r)
     // until e is covered; staged state rows start `halo` positions earlier
-    const int first = ratio * (s / ratio) - halo;
+    const int first = prefill_first(s, ratio, coff);
     const int over = s + n - (first + halo) - tile_rows;
     const int ntile = n == 0 ? 0 : 1 + (over > 0 ? (over + tile_rows - 1) / tile_rows : 0);
     scan[tid] = u;
     scan2[tid] = ntile;
     __syncthreads();
-    for (int off = 1; off < PLAN_THREADS; off <<= 1) {     // inclusive scans
+    for (int off = 1; off < SETUP_THREADS; off <<= 1) {     // inclusive scans
       const int v = tid >= off ? scan[tid - off] : 0;
       const int v2 = tid >= off ? scan2[tid - off] : 0;
       __syncthreads();
@@ -72,7 +106,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
       rec[PL_START] = s;
       rec[PL_NTOK] = n;
       rec[PL_END] = e;
-      rec[PL_ROW0] = row0;
+      rec[PL_ROW0] = q.row0;
       rec[PL_NWIN] = e / ratio - s / ratio;
       rec[PL_NROWS] = u;
       rec[PL_OUT0] = s_carry + scan[tid] - u;
@@ -81,7 +115,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
       rec[PL_NTILE] = ntile;
     }
     __syncthreads();
-    if (tid == PLAN_THREADS - 1) { s_carry += scan[tid]; s_tcarry += scan2[tid]; }
+    if (tid == SETUP_THREADS - 1) { s_carry += scan[tid]; s_tcarry += scan2[tid]; }
     __syncthreads();
   }
   if (my_err) atomicOr(&s_err, my_err);
@@ -91,7 +125,6 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     if (s_carry > out_rows) e |= CMP_DEVERR_OUT_ROWS;
     *err = e;                                       // this call's error word
     *tile_count = s_tcarry;
-    *had_general = 0;                               // set by hadamard_pack_kernel
   }
 }
 
@@ -120,13 +153,13 @@ __device__ __forceinline__ bool row_has_window(const int32_t* __restrict__ plan,
 // times the weight), interleaved RoPE on channels [D-64, D) ([PyPTO]
 // 压缩窗口与状态更新 / 算子级辅助函数), then either the bf16 store or, with
 // rotate, out = y @ Had as a bf16 MFMA product (K = D) against the matrix in
-// fragment-major order (hadamard_pack_kernel).  Rows without a window are +0.
+// fragment-major order (hadamard_pack_block).  Rows without a window are +0.
 // Pairs (2i, 2i+1) of the rotary slice rotate together: the even element with
 // cos/sin column i, the odd one with column 32 + i.
 //
 // Each wave normalises 16 rows in four batches of 4 (all loads of a batch in
 // flight before the first reduction).  When Had is a scaled Sylvester matrix
-// (hadamard_pack_kernel leaves *had_general zero) the product is the fast
+// (no hadamard_pack_block flag is set) the product is the fast
 // Walsh-Hadamard transform of the fp32 row in registers (log2 D butterfly
 // stages: within a lane, then across lanes), times Had[0][0]: no matrix
 // reads.  Otherwise the MFMA product reads each Had fragment once per
@@ -165,7 +198,7 @@ __global__ __launch_bounds__(256) void post_kernel(
     const int32_t* __restrict__ plan, int B, int out_rows,
     const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ cosv,
     const uint16_t* __restrict__ sinv, const uint16_t* __restrict__ hadF,
-    const uint32_t* __restrict__ had_general, uint16_t* __restrict__ out) {
+    const uint32_t* __restrict__ had_flags, int nhad, uint16_t* __restrict__ out) {
   constexpr int D = CPL * 64;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [64][D] bf16, swizzled
   __shared__ int32_t row_live[POST_ROWS];
@@ -191,7 +224,10 @@ __global__ __launch_bounds__(256) void post_kernel(
     }
     row_info[threadIdx.x] = info;
   }
-  __syncthreads();
+  // any Hadamard-check workgroup that found the matrix not a scaled
+  // Sylvester matrix (nhad <= 128 flags, one per thread)
+  const int general = __syncthreads_or(cf.rotate && (int)threadIdx.x < nhad &&
+                                       had_flags[threadIdx.x] != 0);
   const int c0 = lane * CPL;
   const int rope0 = D - cf.rope, half = cf.rope / 2;
   const bool rope_lane = c0 >= rope0;
@@ -199,7 +235,7 @@ __global__ __launch_bounds__(256) void post_kernel(
   float g[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) g[i] = bf2f(gamma[c0 + i]);
-  const bool fwht = cf.rotate && *had_general == 0;
+  const bool fwht = cf.rotate && !general;
   const float hscale = cf.rotate ? bf2f(hadF[0]) : 0.f;   // Had[0][0]
 
 #pragma unroll 1
@@ -392,16 +428,19 @@ __global__ __launch_bounds__(256) void post_kernel(
 // Had (D x D bf16, row k, column n) in the fragment-major order of the MFMA B
 // operand: fragment (column block cb, k-step kk) is 64 lanes x 8 values, lane
 // l holding column cb*32 + l%32 and rows kk*16 + 8*(l/32) .. +8.  One thread
-// per lane piece; D*D/8 pieces.  The same pass checks whether Had is the
-// Sylvester matrix times a constant, Had[k][n] = Had[0][0] * (-1)^popcount(k & n)
-// bit for bit, with Had[0][0] finite and non-zero; any other matrix sets
-// *had_general (cleared by plan_kernel), and post_kernel then multiplies by
-// the matrix instead of running the fast transform.
-__global__ __launch_bounds__(256) void hadamard_pack_kernel(const uint16_t* __restrict__ had,
-                                                            uint16_t* __restrict__ hadF, int D,
-                                                            uint32_t* __restrict__ had_general) {
-  const int o = blockIdx.x * 256 + threadIdx.x;
-  if (o >= D * D / 8) return;
+// per lane piece; D*D/8 pieces, 256 per workgroup.  The same pass checks
+// whether Had is the Sylvester matrix times a constant, Had[k][n] =
+// Had[0][0] * (-1)^popcount(k & n) bit for bit, with Had[0][0] finite and
+// non-zero: workgroup `wg` writes flag[wg] = 1 if its pieces hold any other
+// value, else 0, and post_kernel multiplies by the matrix instead of running
+// the fast transform when any flag is set.
+__device__ __forceinline__ void hadamard_pack_block(int wg, const uint16_t* __restrict__ had,
+                                                    uint16_t* __restrict__ hadF, int D,
+                                                    uint32_t* __restrict__ had_flags) {
+  __shared__ int any_general;
+  if (threadIdx.x == 0) any_general = 0;
+  __syncthreads();
+  const int o = wg * 256 + threadIdx.x;
   const int lane = o & 63, f = o >> 6;
   const int ks = D / 16;
   const int cb = f / ks, kk = f - cb * ks;
@@ -417,7 +456,59 @@ __global__ __launch_bounds__(256) void hadamard_pack_kernel(const uint16_t* __re
   }
   *reinterpret_cast<uint4*>(hadF + (size_t)o * 8) =
       make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
-  if (__ballot(!sylvester) && lane == 0) atomicOr(had_general, 1u);
+  if (!sylvester) any_general = 1;
+  __syncthreads();
+  if (threadIdx.x == 0) had_flags[wg] = any_general ? 1u : 0u;
+}
+
+// Staging of ring row j of request b: position p = first_b + j, when
+// 0 <= p < s_b, into row j of the request's staging area (kv row of coff*D,
+// then the score row).  A table entry outside the pool skips the row; the
+// GEMM reports it (its first tile of the request checks the same entries).
+__device__ __forceinline__ void prefix_block(const Cfg& cf, int j, int b, int B, int T,
+                                             const int32_t* __restrict__ cu_seqlens,
+                                             const int32_t* __restrict__ seqused,
+                                             const int32_t* __restrict__ start_pos,
+                                             const float* __restrict__ kv_state,
+                                             const float* __restrict__ score_state,
+                                             const int32_t* __restrict__ kv_tab,
+                                             const int32_t* __restrict__ st_tab,
+                                             float* __restrict__ staging) {
+  const PReq q = prefill_request(b, B, T, cu_seqlens, seqused, start_pos);
+  const int p = prefill_first(q.s, cf.ratio, cf.coff) + j;
+  if (q.n == 0 || p < 0 || p >= q.s) return;
+  const int cD = cf.coff * cf.D;
+  long rk, rs;
+  if (!state_row(cf, kv_tab, b, p, &rk) || !state_row(cf, st_tab, b, p, &rs)) return;
+  float* dst = staging + ((size_t)b * cf.coff * cf.ratio + j) * 2 * cD;
+  for (int i = threadIdx.x; i < cD; i += blockDim.x) {
+    dst[i] = kv_state[rk * cD + i];
+    dst[cD + i] = score_state[rs * cD + i];
+  }
+}
+
+// The setup launch: workgroup 0 plans, workgroups [1, 1 + nhad) pack the
+// Hadamard matrix (nhad = 0 without rotate), the rest stage ring rows,
+// coff*r per request.
+__global__ __launch_bounds__(SETUP_THREADS) void setup_kernel(
+    Cfg cf, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ seqused,
+    const int32_t* __restrict__ start_pos, int B, int T, int out_rows,
+    int32_t* __restrict__ plan, int32_t* __restrict__ tile_count, uint32_t* __restrict__ err,
+    const uint16_t* __restrict__ had, uint16_t* __restrict__ hadF,
+    uint32_t* __restrict__ had_flags, int nhad, const float* __restrict__ kv_state,
+    const float* __restrict__ score_state, const int32_t* __restrict__ kv_tab,
+    const int32_t* __restrict__ st_tab, float* __restrict__ staging) {
+  const int g = blockIdx.x;
+  if (g == 0) {
+    plan_block(cu_seqlens, seqused, start_pos, B, T, cf.ratio, cf.coff, cf.bm, out_rows, plan,
+               tile_count, err);
+  } else if (g <= nhad) {
+    hadamard_pack_block(g - 1, had, hadF, cf.D, had_flags);
+  } else {
+    const int i = g - 1 - nhad, per = cf.coff * cf.ratio;
+    prefix_block(cf, i % per, i / per, B, T, cu_seqlens, seqused, start_pos, kv_state,
+                 score_state, kv_tab, st_tab, staging);
+  }
 }
 
 // ---------------------------------------------------------------------------

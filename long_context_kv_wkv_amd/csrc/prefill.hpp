@@ -149,7 +149,7 @@ __device__ __forceinline__ bool row_has_window(const int32_t* __restrict__ plan,
 }
 
 // ---------------------------------------------------------------------------
-// Post-processing of 64 output rows per workgroup: RMSNorm (eps 1e-6, fp32,
+// Post-processing of 32 output rows per workgroup: RMSNorm (eps 1e-6, fp32,
 // times the weight), interleaved RoPE on channels [D-64, D) ([PyPTO]
 // 压缩窗口与状态更新 / 算子级辅助函数), then either the bf16 store or, with
 // rotate, out = y @ Had as a bf16 MFMA product (K = D) against the matrix in
@@ -157,16 +157,19 @@ __device__ __forceinline__ bool row_has_window(const int32_t* __restrict__ plan,
 // Pairs (2i, 2i+1) of the rotary slice rotate together: the even element with
 // cos/sin column i, the odd one with column 32 + i.
 //
-// Each wave normalises 16 rows in four batches of 4 (all loads of a batch in
+// Each wave normalises 8 rows in two batches of 4 (all loads of a batch in
 // flight before the first reduction).  When Had is a scaled Sylvester matrix
 // (no hadamard_pack_block flag is set) the product is the fast
 // Walsh-Hadamard transform of the fp32 row in registers (log2 D butterfly
 // stages: within a lane, then across lanes), times Had[0][0]: no matrix
 // reads.  Otherwise the MFMA product reads each Had fragment once per
-// workgroup, four k-steps ahead of its use, and the result goes back through
-// the LDS tile so that the bf16 rows leave as 16-byte stores.
+// 32-column block of a wave, four k-steps ahead of its use, and stores each
+// block's rows as it completes.  Both paths keep the register demand low enough for four waves
+// per SIMD (with 64-row tiles and every output block's accumulators live,
+// the kernel needed 384 registers per wave: one wave per SIMD, and half of
+// the workgroups of a 32768-row call waited for a second round).
 // ---------------------------------------------------------------------------
-constexpr int POST_ROWS = 64;
+constexpr int POST_ROWS = 32;
 constexpr int POST_BATCH = 4;
 
 // N consecutive bf16 rotary columns, loaded as one piece
@@ -193,7 +196,7 @@ __device__ __forceinline__ void fwht_lanes(float (&y)[CPL], int lane) {
 }
 
 template <int CPL>
-__global__ __launch_bounds__(256) void post_kernel(
+__global__ __launch_bounds__(256, 4) void post_kernel(
     Cfg cf, const float* __restrict__ pooled, const float* __restrict__ split,
     const int32_t* __restrict__ plan, int B, int out_rows,
     const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ cosv,
@@ -360,68 +363,53 @@ __global__ __launch_bounds__(256) void post_kernel(
   if (!cf.rotate || fwht) return;
   __syncthreads();
 
-  // out[64, D] = Y[64, D] . Had; wave w owns output columns [w*D/4, (w+1)*D/4)
+  // out[POST_ROWS, D] = Y . Had; wave w owns output columns [w*D/4,
+  // (w+1)*D/4), walked one 32-column block at a time (few accumulators live:
+  // the kernel's register demand sets how many waves share a SIMD on every
+  // path).  The tile is only read, so each block's rows go straight out: 32
+  // lanes write 64 contiguous bytes of one row per store.
+  constexpr int RB = POST_ROWS / 32;        // 32-row blocks of the tile
   constexpr int NB = D / 128;               // 32-column blocks per wave
   constexpr int KS = D / 16;                // k-steps
   constexpr int PF = KS < 4 ? KS : 4;       // k-steps of Had fragments in flight
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int cb0 = wave * NB;
-  const uint16_t* hsrc = hadF + ((size_t)cb0 * KS * 64 + lane) * 8;   // fragment (cb0, 0)
-  f32x16 acc[2][NB];
+#pragma unroll 1
+  for (int j = 0; j < NB; ++j) {
+    const uint16_t* hsrc = hadF + ((size_t)(cb0 + j) * KS * 64 + lane) * 8;   // fragment (cb, 0)
+    f32x16 acc[RB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    bf16x8 bq[PF];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  bf16x8 bq[PF][NB];
+    for (int pf = 0; pf < PF; ++pf) bq[pf] = *reinterpret_cast<const bf16x8*>(hsrc + (size_t)pf * 512);
+    static_assert(KS % PF == 0, "k-steps in whole prefetch rounds");
+#pragma unroll 1
+    for (int k0 = 0; k0 < KS; k0 += PF) {
 #pragma unroll
-  for (int p = 0; p < PF; ++p)
+      for (int pf = 0; pf < PF; ++pf) {
+        const int kk = k0 + pf;
+        const int ch = kk * 2 + lhalf;
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      bq[p][j] = *reinterpret_cast<const bf16x8*>(hsrc + ((size_t)j * KS + p) * 512);
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const int ch = kk * 2 + lhalf;
-    bf16x8 a[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(smem + post_lds<D>(i * 32 + lrow, ch));
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bq[kk % PF][j], acc[i][j], 0, 0, 0);
-    if (kk + PF < KS) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        bq[kk % PF][j] = *reinterpret_cast<const bf16x8*>(hsrc + ((size_t)j * KS + kk + PF) * 512);
-    }
-  }
-  __syncthreads();   // every wave is done reading Y
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-      const bool lv = row_live[lr] != 0;
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int col = (cb0 + j) * 32 + lrow;
-        *reinterpret_cast<uint16_t*>(smem + post_lds<D>(lr, col >> 3) + (col & 7) * 2) =
-            lv ? f2bf(acc[i][j][r]) : uint16_t(0);
+        for (int i = 0; i < RB; ++i) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(smem + post_lds<D>(i * 32 + lrow, ch));
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[pf], acc[i], 0, 0, 0);
+        }
+        if (kk + PF < KS) bq[pf] = *reinterpret_cast<const bf16x8*>(hsrc + (size_t)(kk + PF) * 512);
       }
     }
-  __syncthreads();
-  constexpr int CHUNKS = D / 8;             // 16-byte chunks per row
+    // element r of block i is tile row i*32 + 8*(r/4) + 4*lhalf + r%4
+    const int col = (cb0 + j) * 32 + lrow;
 #pragma unroll
-  for (int it = 0; it < POST_ROWS * CHUNKS / 256; ++it) {
-    const int q = it * 256 + (int)threadIdx.x;
-    const int lr = q / CHUNKS, ch = q - lr * CHUNKS;
-    const int row = row_base + lr;
-    if (row < out_rows)
-      *reinterpret_cast<uint4*>(out + (size_t)row * D + ch * 8) =
-          *reinterpret_cast<const uint4*>(smem + post_lds<D>(lr, ch));
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
+        const int row = row_base + lr;
+        if (row < out_rows) out[(size_t)row * D + col] = row_live[lr] ? f2bf(acc[i][r]) : uint16_t(0);
+      }
   }
 }
 

@@ -156,7 +156,7 @@ PrefillLayout prefill_layout(const Cfg& cf, int T, int B, int out_rows) {
   PrefillLayout L;
   size_t o = 0;
   L.err = 0;
-  L.tiles = 4;    o += 256;                // error word, GEMM tile count
+  L.tiles = 4;    o += 256;                // error word, GEMM tile count, tile queues
   // one "Had is not a scaled Sylvester matrix" flag per packing workgroup
   L.hadflag = o;  o = align256(o + (size_t)hadamard_pack_wgs(cf) * 4);
   L.plan = o;     o = align256(o + (size_t)B * PL_WIDTH * 4);

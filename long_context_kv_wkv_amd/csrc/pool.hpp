@@ -583,15 +583,46 @@ __device__ __forceinline__ void pool_epilogue(
 }
 
 // Persistent kernel: one workgroup per CU walks its tiles.  Workgroup i runs
-// on XCD i % 8; each XCD takes a contiguous run of tiles (N fastest) and its
-// workgroups take every (workgroups per XCD)-th tile of it, so the XCD's
-// co-running tiles share x rows and panel slices in its L2.  While a tile
-// runs its last three K steps, the next tile's first three stages are copied,
-// so its epilogue overlaps the next tile's pipeline fill.
+// on XCD i % 8; each XCD owns a contiguous run of tiles (N fastest), so the
+// XCD's co-running tiles share x rows and panel slices in its L2.  A
+// workgroup's first two tiles are fixed (its slot in the XCD's first two
+// rounds); the rest of the run is a queue: tiles[1 + xcd] counts the tiles
+// taken from it, and a workgroup whose XCD queue is empty takes from the
+// other XCDs' queues.  XCDs run at different clocks under this load (about
+// 10% apart), and a static split left the fastest workgroups idle for the
+// last ~6% of the call.  A workgroup takes the tile after its next one while
+// the current epilogue runs (one lane's atomic, its result passed on through
+// LDS), so the next tile's first three stages are copied while the current
+// tile runs its last three K steps, as in a static walk.
+struct TileQueue {
+  int32_t* heads;   // per-XCD count of tiles taken
+  int per_xcd, first_dyn, total;
+};
+// Tile range of XCD x's queue: [x*per_xcd + first_dyn, min((x+1)*per_xcd, total)).
+__device__ __forceinline__ int queue_take(const TileQueue& q, int x) {
+  const int lo = x * q.per_xcd + q.first_dyn, hi = min((x + 1) * q.per_xcd, q.total);
+  if (lo >= hi) return -1;
+  const int t = lo + atomicAdd(q.heads + x, 1);
+  return t < hi ? t : -1;
+}
+// The other XCDs' queues, in turn, once the own one is empty.
+__device__ __forceinline__ int queue_steal(const TileQueue& q, int xcd) {
+  for (int d = 1; d < 8; ++d) {
+    const int t = queue_take(q, (xcd + d) & 7);
+    if (t >= 0) return t;
+  }
+  return -1;
+}
+// Byte offset in the idle panel stage of the word that passes a taken tile
+// to every wave (past the epilogue's exchange).
+constexpr int GM_QUEUE_SLOT = GM_IDLE_BYTES - 16;
+static_assert(2 * 2 * 64 * sizeof(Soft) <= GM_QUEUE_SLOT && 3 * 2 * 32 * sizeof(Soft) <= GM_QUEUE_SLOT,
+              "the queue word lies past the epilogue exchange");
+
 template <int R, int COFF, int WV>
 __global__ __launch_bounds__(Gm<WV>::THREADS, 1) void gemm_pool_kernel(
     Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int T, int B,
-    const int32_t* __restrict__ plan, const int32_t* __restrict__ tile_count,
+    const int32_t* __restrict__ plan, int32_t* __restrict__ tiles,
     const float* __restrict__ ape, const float* __restrict__ staging,
     float* __restrict__ kv_state, float* __restrict__ score_state,
     const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
@@ -600,13 +631,16 @@ __global__ __launch_bounds__(Gm<WV>::THREADS, 1) void gemm_pool_kernel(
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   uint8_t* xch = smem + GM_IDLE_OFF;
   const int tiles_n = cf.N / GM_BN;
-  const int total = *tile_count * tiles_n;
+  const int total = tiles[0] * tiles_n;
   const int per_wg = gridDim.x >> 3;                // workgroups per XCD
   const int per_xcd = (total + 7) >> 3;             // tiles per XCD
-  const int lo = (blockIdx.x & 7) * per_xcd;
+  const int xcd = blockIdx.x & 7;
+  const int lo = xcd * per_xcd;
   const int hi = min(lo + per_xcd, total);
+  const TileQueue q{tiles + 1, per_xcd, 2 * per_wg, total};
   int tile = lo + (blockIdx.x >> 3);
   if (tile >= hi) return;
+  int next = tile + per_wg < hi ? tile + per_wg : -1;
   const int KT = cf.H / GM_BK, ksteps = cf.H >> 4;
   PoolTile cur = pool_tile<R, Gm<WV>::BM>(tile, tiles_n, plan, B);
   GmSrc csrc = pool_sources<WV>(cur, cf, X, W, T);
@@ -615,15 +649,28 @@ __global__ __launch_bounds__(Gm<WV>::THREADS, 1) void gemm_pool_kernel(
   const int xstep = (KT >> 1) % 3;   // X buffer rotation per tile
   int xrot = 0;
   while (true) {
-    const int next = tile + per_wg;
-    const bool has_next = next < hi;
+    const bool has_next = next >= 0;
     const PoolTile nxt = has_next ? pool_tile<R, Gm<WV>::BM>(next, tiles_n, plan, B) : cur;
     const GmSrc nsrc = has_next ? pool_sources<WV>(nxt, cf, X, W, T) : csrc;
     gemm_tile_any<WV>(acc, smem, csrc, nsrc, has_next, KT, xrot, ksteps);
+    // the tile after the next one: taken now, read after the epilogue
+    int taken = -1;
+    if (has_next && threadIdx.x == 0) taken = queue_take(q, xcd);
     pool_epilogue<R, COFF, WV>(cf, acc, xch, cur, ape, staging, kv_state, score_state, kv_tab,
                            st_tab, pooled, out_rows, split, err);
     if (!has_next) break;
-    tile = next;
+    if (threadIdx.x == 0) {
+      if (taken < 0) taken = queue_steal(q, xcd);
+      *reinterpret_cast<volatile int*>(xch + GM_QUEUE_SLOT) = taken;
+    }
+    // a bare barrier (a workgroup fence would also wait for the next tile's
+    // copies in flight); the slot is read before the next K loop's copies
+    // can reach the idle stage
+    __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    const int after = __builtin_amdgcn_readfirstlane(
+        *reinterpret_cast<volatile int*>(xch + GM_QUEUE_SLOT));
+    next = after;
     cur = nxt;
     // rebuild the copy sources rather than carry them through the epilogue,
     // whose register demand would spill them (an opaque tile field keeps the

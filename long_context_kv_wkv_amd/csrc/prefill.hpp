@@ -8,7 +8,8 @@ namespace cmp {
 // ---------------------------------------------------------------------------
 // Setup of a prefill call: one launch of three independent parts.
 //  * workgroup 0 plans the call (per-request start, length, windows, output
-//    rows and GEMM tiles) and writes the call's error word;
+//    rows and GEMM tiles), writes the call's error word and clears the
+//    GEMM's tile queue heads;
 //  * the next D*D/2048 workgroups (rotate only) check the Hadamard matrix
 //    and copy it to the MFMA fragment order;
 //  * the rest stage the ring rows of positions before each request's first
@@ -124,8 +125,9 @@ __device__ __forceinline__ void plan_block(
     uint32_t e = s_err;
     if (s_carry > out_rows) e |= CMP_DEVERR_OUT_ROWS;
     *err = e;                                       // this call's error word
-    *tile_count = s_tcarry;
+    tile_count[0] = s_tcarry;
   }
+  if (tid >= 1 && tid <= 8) tile_count[tid] = 0;   // the GEMM's per-XCD tile queues
 }
 
 // Request owning output row `row` (largest b with o_b <= row), or -1.

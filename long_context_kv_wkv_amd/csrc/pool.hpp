@@ -324,21 +324,29 @@ __device__ __forceinline__ PoolTile pool_tile(int tile, int tiles_n, const int32
   return t;
 }
 
-// The tile's copy sources: X rows of positions P0 + (tile row), clamped into x.
+// The tile's copy sources for copy role `role`: X rows of positions
+// P0 + (tile row), clamped into x.
 template <int WV>
 __device__ __forceinline__ GmSrc pool_sources(const PoolTile& t, const Cfg& cf,
                                               const uint16_t* __restrict__ X,
-                                              const uint16_t* __restrict__ W, int T) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                                              const uint16_t* __restrict__ W, int T, int role) {
+  const int lane = threadIdx.x & 63;
   const int s = t.rec[PL_START], row0 = t.rec[PL_ROW0];
   int arow[GM_A_COPIES];
 #pragma unroll
   for (int j = 0; j < GM_A_COPIES; ++j) {
-    const int p = t.P0 + gm_copy_row(wave, lane, j);
+    const int p = t.P0 + gm_copy_row(role, lane, j);
     arow[j] = min(max(row0 + (p - s), 0), T - 1);
   }
-  return gm_sources<WV>(X, W, cf.H, t.n0, arow, min(max(row0 + (t.P0 - s), 0), T - 1));
+  return gm_sources<WV>(X, W, cf.H, t.n0, arow, min(max(row0 + (t.P0 - s), 0), T - 1), role);
 }
+
+// Workgroup barriers one pool_epilogue call passes, on every path: the
+// exchange between row-waves (ratio 4, and windows that span two row-waves).
+// The copy waves of the 4-wave shape pass the same number instead of running
+// the epilogue.
+template <int R, int COFF>
+constexpr int epilogue_barriers() { return COFF == 2 || R > GM_WROWS ? 1 : 0; }
 
 // Pooling epilogue of one tile (see the top of this file).  xch: LDS (at most
 // 3 KiB used) that no copy fills and no K loop reads while the epilogue runs.
@@ -619,6 +627,76 @@ constexpr int GM_QUEUE_SLOT = GM_IDLE_BYTES - 16;
 static_assert(2 * 2 * 64 * sizeof(Soft) <= GM_QUEUE_SLOT && 3 * 2 * 32 * sizeof(Soft) <= GM_QUEUE_SLOT,
               "the queue word lies past the epilogue exchange");
 
+// The tile walk of one wave in role MODE (GmMode); copy role `role`.  Every
+// role passes the same barriers: the K loop's, the epilogue's (a copy wave
+// passes epilogue_barriers() instead of running it) and the one that hands
+// on each taken tile.  One instance per role keeps each role's registers
+// apart (a single walk branching per tile spilled the MFMA loop's
+// addresses).
+template <int R, int COFF, int WV, int MODE>
+__device__ __forceinline__ void pool_walk(
+    const Cfg& cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int T, int B,
+    const int32_t* __restrict__ plan, const TileQueue& q, int xcd, int tile, int next,
+    const float* __restrict__ ape, const float* __restrict__ staging,
+    float* __restrict__ kv_state, float* __restrict__ score_state,
+    const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
+    float* __restrict__ pooled, int out_rows, float* __restrict__ split,
+    uint32_t* __restrict__ err, uint8_t* smem, int role) {
+  constexpr bool COPY = MODE != GM_MFMA, MUL = MODE != GM_COPY;
+  uint8_t* xch = smem + GM_IDLE_OFF;
+  const int tiles_n = cf.N / GM_BN;
+  const int KT = cf.H / GM_BK, ksteps = cf.H >> 4;
+  PoolTile cur = pool_tile<R, Gm<WV>::BM>(tile, tiles_n, plan, B);
+  GmSrc csrc{};
+  if constexpr (COPY) {
+    csrc = pool_sources<WV>(cur, cf, X, W, T, role);
+    gm_prologue<WV>(smem, csrc, ksteps, role);
+  }
+  f32x16 acc[2][4];
+  const int xstep = (KT >> 1) % 3;   // X buffer rotation per tile
+  int xrot = 0;
+  while (true) {
+    const bool has_next = next >= 0;
+    const PoolTile nxt = has_next ? pool_tile<R, Gm<WV>::BM>(next, tiles_n, plan, B) : cur;
+    GmSrc nsrc{};
+    if constexpr (COPY) nsrc = has_next ? pool_sources<WV>(nxt, cf, X, W, T, role) : csrc;
+    gemm_tile_any<WV, MODE>(acc, smem, csrc, nsrc, has_next, KT, xrot, ksteps, role);
+    // the tile after the next one: taken now, read after the epilogue
+    int taken = -1;
+    if constexpr (MUL) {
+      if (has_next && threadIdx.x == 0) taken = queue_take(q, xcd);
+      pool_epilogue<R, COFF, WV>(cf, acc, xch, cur, ape, staging, kv_state, score_state, kv_tab,
+                                 st_tab, pooled, out_rows, split, err);
+    } else {
+#pragma unroll
+      for (int i = 0; i < epilogue_barriers<R, COFF>(); ++i) asm volatile("s_barrier" ::: "memory");
+    }
+    if (!has_next) break;
+    if (MUL && threadIdx.x == 0) {
+      if (taken < 0) taken = queue_steal(q, xcd);
+      *reinterpret_cast<volatile int*>(xch + GM_QUEUE_SLOT) = taken;
+    }
+    // a bare barrier (a workgroup fence would also wait for the next tile's
+    // copies in flight); the slot is read before the next K loop's copies
+    // can reach the idle stage
+    __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    next = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(xch + GM_QUEUE_SLOT));
+    cur = nxt;
+    if constexpr (COPY) {
+      // rebuild the copy sources rather than carry them through the
+      // epilogue, whose register demand would spill them (an opaque tile
+      // field keeps the compiler from reusing the values computed before the
+      // K loop)
+      cur.P0 = __builtin_amdgcn_readfirstlane(cur.P0);
+      asm volatile("" : "+s"(cur.P0));
+      csrc = pool_sources<WV>(cur, cf, X, W, T, role);
+    }
+    xrot += xstep;
+    if (xrot >= 3) xrot -= 3;
+  }
+}
+
 template <int R, int COFF, int WV>
 __global__ __launch_bounds__(Gm<WV>::THREADS, 1) void gemm_pool_kernel(
     Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int T, int B,
@@ -629,7 +707,6 @@ __global__ __launch_bounds__(Gm<WV>::THREADS, 1) void gemm_pool_kernel(
     float* __restrict__ pooled, int out_rows, float* __restrict__ split,
     uint32_t* __restrict__ err) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  uint8_t* xch = smem + GM_IDLE_OFF;
   const int tiles_n = cf.N / GM_BN;
   const int total = tiles[0] * tiles_n;
   const int per_wg = gridDim.x >> 3;                // workgroups per XCD
@@ -638,48 +715,22 @@ __global__ __launch_bounds__(Gm<WV>::THREADS, 1) void gemm_pool_kernel(
   const int lo = xcd * per_xcd;
   const int hi = min(lo + per_xcd, total);
   const TileQueue q{tiles + 1, per_xcd, 2 * per_wg, total};
-  int tile = lo + (blockIdx.x >> 3);
+  const int tile = lo + (blockIdx.x >> 3);
   if (tile >= hi) return;
-  int next = tile + per_wg < hi ? tile + per_wg : -1;
-  const int KT = cf.H / GM_BK, ksteps = cf.H >> 4;
-  PoolTile cur = pool_tile<R, Gm<WV>::BM>(tile, tiles_n, plan, B);
-  GmSrc csrc = pool_sources<WV>(cur, cf, X, W, T);
-  gm_prologue<WV>(smem, csrc, ksteps);
-  f32x16 acc[2][4];
-  const int xstep = (KT >> 1) % 3;   // X buffer rotation per tile
-  int xrot = 0;
-  while (true) {
-    const bool has_next = next >= 0;
-    const PoolTile nxt = has_next ? pool_tile<R, Gm<WV>::BM>(next, tiles_n, plan, B) : cur;
-    const GmSrc nsrc = has_next ? pool_sources<WV>(nxt, cf, X, W, T) : csrc;
-    gemm_tile_any<WV>(acc, smem, csrc, nsrc, has_next, KT, xrot, ksteps);
-    // the tile after the next one: taken now, read after the epilogue
-    int taken = -1;
-    if (has_next && threadIdx.x == 0) taken = queue_take(q, xcd);
-    pool_epilogue<R, COFF, WV>(cf, acc, xch, cur, ape, staging, kv_state, score_state, kv_tab,
-                           st_tab, pooled, out_rows, split, err);
-    if (!has_next) break;
-    if (threadIdx.x == 0) {
-      if (taken < 0) taken = queue_steal(q, xcd);
-      *reinterpret_cast<volatile int*>(xch + GM_QUEUE_SLOT) = taken;
-    }
-    // a bare barrier (a workgroup fence would also wait for the next tile's
-    // copies in flight); the slot is read before the next K loop's copies
-    // can reach the idle stage
-    __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
-    const int after = __builtin_amdgcn_readfirstlane(
-        *reinterpret_cast<volatile int*>(xch + GM_QUEUE_SLOT));
-    next = after;
-    cur = nxt;
-    // rebuild the copy sources rather than carry them through the epilogue,
-    // whose register demand would spill them (an opaque tile field keeps the
-    // compiler from reusing the values computed before the K loop)
-    cur.P0 = __builtin_amdgcn_readfirstlane(cur.P0);
-    asm volatile("" : "+s"(cur.P0));
-    csrc = pool_sources<WV>(cur, cf, X, W, T);
-    xrot += xstep;
-    if (xrot >= 3) xrot -= 3;
+  const int next = tile + per_wg < hi ? tile + per_wg : -1;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (Gm<WV>::COPIERS == 0) {
+    pool_walk<R, COFF, WV, GM_ALL>(cf, X, W, T, B, plan, q, xcd, tile, next, ape, staging,
+                                   kv_state, score_state, kv_tab, st_tab, pooled, out_rows, split,
+                                   err, smem, wave);
+  } else if (wave >= WV) {
+    pool_walk<R, COFF, WV, GM_COPY>(cf, X, W, T, B, plan, q, xcd, tile, next, ape, staging,
+                                    kv_state, score_state, kv_tab, st_tab, pooled, out_rows, split,
+                                    err, smem, wave - WV);
+  } else {
+    pool_walk<R, COFF, WV, GM_MFMA>(cf, X, W, T, B, plan, q, xcd, tile, next, ape, staging,
+                                    kv_state, score_state, kv_tab, st_tab, pooled, out_rows, split,
+                                    err, smem, wave);
   }
   gm_drain();
 }

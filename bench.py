@@ -66,7 +66,10 @@ def bench_prefill(steps, warmup, name="c4a_128k", prepared=None):
     for _ in range(warmup):
         case.prefill()
     torch.cuda.synchronize()
-    # the timed steps run without per-kernel events
+    # the timed steps themselves give the per-kernel durations: while timing
+    # is on, the library brackets every launch with HIP events on the stream
+    # it launches on (about 0.5% on the 128K call's time, included in it)
+    cmp.compressor_timing_enable(True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for _ in range(steps):
@@ -74,16 +77,11 @@ def bench_prefill(steps, warmup, name="c4a_128k", prepared=None):
     ev1.record()
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
-    # per-kernel breakdown: a separate pass with every launch bracketed by
-    # events on the library's stream
-    cmp.compressor_timing_enable(True)
-    for _ in range(max(1, min(steps, 10))):
-        case.prefill()
-    torch.cuda.synchronize()
     kernels = {}
     for k in ("setup", "gemm", "post"):
         n, ms = cmp.compressor_timing_query(k)
         if n:
+            assert n == steps, (k, n, steps)
             kernels[k] = ms / n
     cmp.compressor_timing_enable(False)
     windows = w["T"] // w["ratio"]
@@ -369,6 +367,10 @@ def parity_stats(pre, res, rows):
 # Profile summaries (run on the host after the rocprofv3 runs listed in
 # PROFILE_COMMANDS; they read the CSV files those runs leave under a folder)
 # ---------------------------------------------------------------------------
+# the secondary prefill workloads (timed steps each) and their warm-up calls
+OTHER_PREFILL = (("c128a_8192", 200), ("varlen_c4a", 100))
+OTHER_WARMUP = 10
+
 PROFILE_COMMANDS = {
     "kt": "rocprofv3 --kernel-trace --stats -T --output-format csv -d {out}/kt -o run -- "
           "python3 bench.py --steps 20 --warmup 15 --decode-steps 50 --no-cpu-baseline",
@@ -376,6 +378,11 @@ PROFILE_COMMANDS = {
              "python3 bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline",
     "write": "rocprofv3 --pmc WRITE_SIZE -T --output-format csv -d {out}/write -o run -- "
              "python3 bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline",
+    # GPU clock (GUI-active cycles per XCC over the dispatch's duration) and
+    # matrix-core busy cycles of the 128K C4A GEMM
+    "mfma": "rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+            "-T --output-format csv -d {out}/mfma -o run -- "
+            "python3 bench.py --steps 10 --warmup 15 --no-decode --no-cpu-baseline",
     "dkt": "rocprofv3 --kernel-trace --stats -T --output-format csv -d {out}/dkt -o run -- "
            "python3 bench.py --decode-only --decode-workloads decode_c4a,decode_c128a "
            "--decode-steps 100",
@@ -419,9 +426,11 @@ def summarize_profiles(out):
     lines = ["# Kernel-time summary: bench.py (128K C4A prefill + 32-request decode)", "",
              "Command (from the repository root, on one MI355X):", "", "```",
              PROFILE_COMMANDS["kt"].format(out="gpurun_out"), "```", "",
-             "The prefill kernels run 45 times (15 warm-up + 20 timed; the per-kernel event "
-             "pass adds 10 more); the decode kernels run for each decode workload x (warm-up + "
-             "timed + event-timed) steps.  Durations in ns.", "",
+             "The 128K C4A prefill kernels run 35 times (15 warm-up + 20 timed, the timed "
+             "ones with per-kernel events); the other prefill workloads run before it ("
+             + ", ".join(f"{n}: {OTHER_WARMUP} warm-up + {k} timed" for n, k in OTHER_PREFILL)
+             + "); the decode kernels run for each decode workload x (warm-up + timed + "
+             "event-timed) steps.  Durations in ns.", "",
              "| kernel | calls | total ns | average ns | % | min ns | max ns |",
              "|---|---|---|---|---|---|---|"]
     for r in rows:
@@ -437,21 +446,25 @@ def summarize_profiles(out):
              if GEMM_KERNEL in r["Kernel_Name"]]
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
-    # the other prefill workloads run first (each 5 warm-up + 10 timed + 10 in
-    # the event pass); the command's 128K C4A launches come last: 15 warm-up,
-    # 20 timed and 10 in the per-kernel event pass
-    n_head = 15 + 20 + 10
-    if len(dur) >= n_head:
-        rest, head = dur[:-n_head], dur[-n_head:]
+    # the other prefill workloads run first; the command's 128K C4A launches
+    # come last: 15 warm-up and 20 timed (the launches bench.py's roofline
+    # times)
+    n_head = 15 + 20
+    n_other = [OTHER_WARMUP + k for _, k in OTHER_PREFILL]
+    if len(dur) == n_head + sum(n_other):
+        head = dur[-n_head:]
         lines += ["", f"`{GEMM_KERNEL}` per launch of the 128K C4A prefill (ms, from the kernel "
                   "trace, in launch order): " + ", ".join(f"{x:.3f}" for x in head) + ".",
-                  f"Average after the 15 warm-up launches: {np.mean(head[15:]):.3f} ms; average "
-                  f"of its last 10 (the per-kernel event pass that bench.py's roofline times): "
-                  f"{np.mean(head[-10:]):.3f} ms."]
-        if rest:
-            lines += ["", "Earlier launches (the 8192-token C128A prefill, then the packed "
-                      "variable-length C4A prefill, each warm-up + timed + event pass; ms): "
-                      + ", ".join(f"{x:.3f}" for x in rest) + "."]
+                  f"Average of the 20 timed launches (after the 15 warm-up ones): "
+                  f"{np.mean(head[15:]):.3f} ms; median {np.median(head[15:]):.3f} ms."]
+        at = 0
+        for (name, k), n in zip(OTHER_PREFILL, n_other):
+            d = dur[at:at + n]
+            at += n
+            lines += ["", f"`{GEMM_KERNEL}` of {name}: first {OTHER_WARMUP} launches (ms) "
+                      + ", ".join(f"{x:.3f}" for x in d[:OTHER_WARMUP])
+                      + f"; the {k} timed launches: median {np.median(d[OTHER_WARMUP:]):.4f} ms, "
+                      f"min {np.min(d[OTHER_WARMUP:]):.4f}, max {np.max(d[OTHER_WARMUP:]):.4f}."]
     lines += ["", f"Kernel source hash (gemm.hpp + pool.hpp + common.hpp): `{sha}`."]
     open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w").write("\n".join(lines) + "\n")
 
@@ -484,8 +497,61 @@ def summarize_profiles(out):
               indent=1)
     if os.path.isdir(os.path.join(out, "dkt")):
         summarize_decode(out, fscale, wscale)
+    if os.path.isdir(os.path.join(out, "mfma")):
+        summarize_mfma(out, sha)
     print(json.dumps({"kernel_stats_rows": len(rows), "hbm_bytes_per_launch": fb + wb,
                       "sha": sha}))
+
+
+def summarize_mfma(out, sha):
+    """profiles/gemm_c4a_128k_mfma.md: per launch of the 128K C4A GEMM, the
+    GPU clock (GRBM_GUI_ACTIVE cycles per XCC over the dispatch's duration),
+    the matrix cores' busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over GUI-active
+    cycles x 1024 SIMDs) and the bf16 MFMA work the counters saw."""
+    import csv
+    import workloads
+    w = workloads.build_named("c4a_128k", with_x=False)
+    flops = 2.0 * w["T"] * w["hidden"] * 2 * w["coff"] * w["head_dim"]
+    per = {}
+    for r in csv.DictReader(open(_find_csv(os.path.join(out, "mfma"), "counter_collection.csv"))):
+        if GEMM_KERNEL not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]),
+                           {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    rows = [per[k] for k in sorted(per)]
+    # the 128K launches are the ones with the call's full MFMA work
+    rows = [d for d in rows if abs(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 - flops) < 1e-3 * flops]
+    lines = ["# 128K C4A prefill GEMM: clock and matrix-core busy cycles", "",
+             "Command (from the repository root, on one MI355X):", "", "```",
+             PROFILE_COMMANDS["mfma"].format(out="gpurun_out"), "```", "",
+             "Per launch of `gemm_pool_kernel` (15 warm-up + 10 timed, in launch order). "
+             "clock = GRBM_GUI_ACTIVE / 8 XCCs / duration; MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (GUI-active cycles per XCC x 1024 SIMDs); "
+             "MFMA work = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flop.", "",
+             "| launch | duration ms | clock GHz | MFMA busy | MFMA work TFLOP | TFLOP/s | "
+             "of the dense peak at this clock |",
+             "|---|---|---|---|---|---|---|"]
+    for i, d in enumerate(rows):
+        ms = d["ns"] / 1e6
+        cyc = d["GRBM_GUI_ACTIVE"] / 8.0
+        ghz = cyc / d["ns"]
+        busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024)
+        work = d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        tf = work / (ms * 1e-3) / 1e12
+        lines.append(f"| {i} | {ms:.3f} | {ghz:.3f} | {busy * 100:.1f}% | {work / 1e12:.4f} | "
+                     f"{tf:.0f} | {tf / (PEAK_BF16_TFLOPS * ghz / 2.4) * 100:.1f}% |")
+    if rows:
+        last = rows[-10:]
+        ghz = np.mean([d["GRBM_GUI_ACTIVE"] / 8.0 / d["ns"] for d in last])
+        busy = np.mean([d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / 8.0 * 1024)
+                        for d in last])
+        lines += ["", f"Last 10 launches: clock {ghz:.3f} GHz, MFMA busy {busy * 100:.1f}% of "
+                  f"the cycles; the dense bf16 peak at that clock is "
+                  f"{PEAK_BF16_TFLOPS * ghz / 2.4:.0f} TFLOP/s (2500 at 2.4 GHz).  The "
+                  f"algorithmic work is {flops / 1e12:.4f} TFLOP per launch."]
+    lines += ["", f"Kernel source hash (gemm.hpp + pool.hpp + common.hpp): `{sha}`."]
+    open(os.path.join(ROOT, "profiles", "gemm_c4a_128k_mfma.md"), "w").write("\n".join(lines) + "\n")
 
 
 def summarize_decode(out, fscale, wscale):
@@ -562,8 +628,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # the first ~10 calls of the 128K prefill run slower while clocks and
-    # translation caches settle; the default warm-up covers that ramp
+    # the first ~10 calls of the 128K prefill run slower while the clocks
+    # settle; the default warm-up covers that ramp
     ap.add_argument("--warmup", type=int, default=15)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -612,7 +678,7 @@ def main():
     head_case = prepare_prefill("c4a_128k")
     other_cases = {}
     if not a.no_decode:
-        for name in ("c128a_8192", "varlen_c4a"):
+        for name, _ in OTHER_PREFILL:
             other_cases[name] = prepare_prefill(name)
     progress("inputs drawn and uploaded")
     extra = {}
@@ -641,8 +707,8 @@ def main():
         # the other prefill workloads: the 8192-token C128A call and the
         # packed variable-length C4A continuation (8 requests, 88826 tokens)
         other = {}
-        for name, steps in (("c128a_8192", 200), ("varlen_c4a", 100)):
-            p = bench_prefill(steps, 10, name, prepared=other_cases.pop(name))
+        for name, steps in OTHER_PREFILL:
+            p = bench_prefill(steps, OTHER_WARMUP, name, prepared=other_cases.pop(name))
             progress(f"{name}: {p['ms_per_step']:.3f} ms per call")
             pw = p["w"]
             fl = 2.0 * pw["T"] * pw["hidden"] * 2 * pw["coff"] * pw["head_dim"]

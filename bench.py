@@ -70,13 +70,14 @@ def bench_prefill(steps, warmup, name="c4a_128k", prepared=None):
     # is on, the library brackets every launch with HIP events on the stream
     # it launches on (about 0.5% on the 128K call's time, included in it)
     cmp.compressor_timing_enable(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(steps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
         case.prefill()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
+    total_ms = evs[0].elapsed_time(evs[-1])
+    per_call = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
     kernels = {}
     for k in ("setup", "gemm", "post"):
         n, ms = cmp.compressor_timing_query(k)
@@ -88,6 +89,9 @@ def bench_prefill(steps, warmup, name="c4a_128k", prepared=None):
     out_bits = case.out_bits().copy()
     kv, sc = case.states()
     return dict(w=w, ms_per_step=total_ms / steps, windows=windows, kernels=kernels,
+                ms_per_call={"median": float(np.median(per_call)),
+                             "p10": float(np.percentile(per_call, 10)),
+                             "p90": float(np.percentile(per_call, 90))},
                 device=torch.cuda.get_device_name(0), out_bits=out_bits, kv=kv.copy(),
                 sc=sc.copy())
 
@@ -181,6 +185,49 @@ def bench_decode(name, steps, warmup, copies=12):
     panel_bytes = case.w_packed.numel() * 2
     return dict(us_per_step=us, us_per_step_eager=us_eager, kernels_us=kern,
                 panel_bytes=panel_bytes, step_bytes=decode_bytes(w))
+
+
+def bench_reference(T=131072, H=7168, N=2048, reps=10):
+    """Context for the roofline, measured on the same GPU: the vendor
+    library's plain bf16 GEMM of the 128K C4A projection's shape (torch.mm:
+    no pooling, bf16 output) on N(0,1) data, and a plain 1 GiB device copy."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20262)
+    a = torch.randn((T, H), device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn((N, H), device="cuda", dtype=torch.bfloat16, generator=g).t().contiguous()
+    c = torch.empty((T, N), device="cuda", dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    mm_ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    cp_ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"torch_mm_same_shape_ms": mm_ms,
+            "torch_mm_same_shape_tflops": 2.0 * T * H * N / (mm_ms * 1e-3) / 1e12,
+            "copy_1GiB_GBps": 2.0 * (1 << 30) / (cp_ms * 1e-3) / 1e9,
+            "note": "vendor bf16 GEMM (torch.mm, hipBLASLt) of the shape x[131072, 7168] . "
+                    "W[2048, 7168]^T with bf16 output and no pooling, N(0,1) inputs; device copy "
+                    "of 1 GiB (read + write bytes)"}
 
 
 def bench_epilog(steps, copies=9):
@@ -712,11 +759,14 @@ def main():
             progress(f"{name}: {p['ms_per_step']:.3f} ms per call")
             pw = p["w"]
             fl = 2.0 * pw["T"] * pw["hidden"] * 2 * pw["coff"] * pw["head_dim"]
-            other[name] = {"ms_per_step": p["ms_per_step"], "kernels_ms": p["kernels"],
+            other[name] = {"ms_per_step": p["ms_per_step"], "ms_per_call": p["ms_per_call"],
+                           "kernels_ms": p["kernels"],
                            "gemm_tflops": fl / (p["kernels"]["gemm"] * 1e-3) / 1e12,
                            "gemm_mfma_frac": fl / (p["kernels"]["gemm"] * 1e-3) / 1e12
                            / PEAK_BF16_TFLOPS, "tokens": pw["T"]}
         extra["prefill_other"] = other
+        extra["reference"] = bench_reference()
+        progress("reference GEMM and copy done")
     pre = bench_prefill(a.steps, a.warmup, prepared=head_case)
     progress(f"c4a_128k: {pre['ms_per_step']:.3f} ms per call")
     w = pre["w"]
@@ -744,6 +794,7 @@ def main():
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": gemm_ms,
                      "whole_call_frac": flops / (pre["ms_per_step"] * 1e-3) / 1e12
                      / PEAK_BF16_TFLOPS},
+        "ms_per_call": pre["ms_per_call"],
         "kernels_ms": pre["kernels"],
         "device": pre["device"],
     }

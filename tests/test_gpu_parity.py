@@ -120,6 +120,21 @@ def test_prefill_hadamard_matrix_kinds(harness, kind, D):
     assert case.device_error() == 0
 
 
+def test_varlen_mid_size(harness, tile_rows):
+    """About 20K packed tokens (8 requests): enough tiles that each XCD's
+    run has a fixed part (every workgroup's first two tiles) and a queued
+    part, at either tile height."""
+    _announce(f"varlen mid size, tile rows {tile_rows}")
+    w = _varlen_small("varlen_mid", 5000, pad=3)
+    assert w["T"] > 12000
+    case, res = _run_prefill(harness, w)
+    mx, mae = assert_out(case.out_bits(), res)
+    kv, sc = case.states()
+    assert_states(kv, sc, w, res)
+    assert case.device_error() == 0
+    print(f"varlen mid T={w['T']} tile rows {tile_rows}: max scaled err {mx:.2e}, MAE {mae:.2e}")
+
+
 # oracle results of the full-size workloads, computed once for both tile heights
 _FULL = {}
 

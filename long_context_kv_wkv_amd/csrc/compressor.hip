@@ -149,8 +149,11 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 inline int hadamard_pack_wgs(const Cfg& cf) { return cf.rotate ? cf.D * cf.D / 8 / 256 : 0; }
 
 struct PrefillLayout {
-  size_t err, tiles, hadflag, plan, pooled, hadF, staging, split, total;
+  size_t err, tiles, hadflag, plan, pooled, hadF, apet, staging, split, total;
 };
+// Workgroups of the setup launch that copy Ape transposed: ratios >= 8
+// (coff = 1), R/4 slots each.
+int ape_transpose_wgs(const Cfg& cf) { return cf.ratio >= 8 ? cf.ratio / 4 : 0; }
 int prefill_max_tiles(int T, int B, int bm);
 PrefillLayout prefill_layout(const Cfg& cf, int T, int B, int out_rows) {
   PrefillLayout L;
@@ -162,6 +165,7 @@ PrefillLayout prefill_layout(const Cfg& cf, int T, int B, int out_rows) {
   L.plan = o;     o = align256(o + (size_t)B * PL_WIDTH * 4);
   L.pooled = o;   o = align256(o + (size_t)out_rows * cf.D * 4);
   L.hadF = o;     o = align256(o + (cf.rotate ? (size_t)cf.D * cf.D * 2 : 0));
+  L.apet = o;     o = align256(o + (size_t)ape_transpose_wgs(cf) * 4 * cf.coff * cf.D * 4);
   L.staging = o;  o = align256(o + (size_t)B * cf.coff * cf.ratio * 2 * cf.coff * cf.D * 4);
   // sized for the shorter tiles, whichever the call runs
   L.split = o;    o = align256(o + (cf.coff == 2 ? (size_t)prefill_max_tiles(T, B, 128) * 6 * cf.D * 4 : 0));
@@ -465,6 +469,7 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
   float* pooled = reinterpret_cast<float*>(ws + L.pooled);
   uint16_t* hadF = reinterpret_cast<uint16_t*>(ws + L.hadF);
   float* staging = reinterpret_cast<float*>(ws + L.staging);
+  float* apet = reinterpret_cast<float*>(ws + L.apet);
   float* split = reinterpret_cast<float*>(ws + L.split);
   const int32_t* kvt = a->kv_block_table ? a->kv_block_table : a->state_block_table;
   const int B = a->batch, T = a->T;
@@ -476,12 +481,14 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
   cf.bm = forced ? forced : (long)((T + 255) / 256) * tiles_n < cus ? 128 : 256;
 
   const int nhad = hadamard_pack_wgs(cf);
+  const int napet = T > 0 ? ape_transpose_wgs(cf) : 0;
   const int nstage = T > 0 ? B * cf.coff * cf.ratio : 0;
   CMP_TRY(launch("setup", st, [&] {
-    hipLaunchKernelGGL(setup_kernel, dim3(1 + nhad + nstage), dim3(SETUP_THREADS), 0, st, cf,
-                       a->cu_seqlens, a->seqused, a->start_pos, B, T, a->out_rows, plan, tiles,
+    hipLaunchKernelGGL(setup_kernel, dim3(1 + nhad + napet + nstage), dim3(SETUP_THREADS), 0, st,
+                       cf, a->cu_seqlens, a->seqused, a->start_pos, B, T, a->out_rows, plan, tiles,
                        err, static_cast<const uint16_t*>(a->hadamard), hadF, had_flags, nhad,
-                       a->kv_state, a->score_state, kvt, a->state_block_table, staging);
+                       a->ape, apet, napet, a->kv_state, a->score_state, kvt,
+                       a->state_block_table, staging);
   }));
   if (T > 0) {
     // persistent: one workgroup per CU (a multiple of 8, one run of tiles
@@ -499,8 +506,8 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
       hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, cf,
                          static_cast<const uint16_t*>(a->x),
                          static_cast<const uint16_t*>(a->w_packed), T, B, plan, tiles, a->ape,
-                         staging, a->kv_state, a->score_state, kvt, a->state_block_table, pooled,
-                         a->out_rows, split, err);
+                         apet, staging, a->kv_state, a->score_state, kvt, a->state_block_table,
+                         pooled, a->out_rows, split, err);
     }));
   }
   if (a->out_rows > 0) {

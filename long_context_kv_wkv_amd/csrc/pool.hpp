@@ -134,6 +134,7 @@ struct EpiCtx {
   int s, e, live_lo, first;
   const float* stg;    // staged ring rows of positions [first, s)
   const float* ape;
+  const float* apet;   // Ape transposed, [channel][slot] (ratio >= 8)
   int c0, c1, h;
   int orow0;           // output row of the wave's first window, if complete
   int wfirst, wend, wg0;
@@ -143,18 +144,23 @@ struct EpiCtx {
   int wm, wn;
 };
 
-// value of channel c of (kv or score) at wave row jr: accumulator, Ape, or
-// the staged row for positions before the call; false if no token there
+// slot of wave row jr in its window (the wave starts a window unless a
+// window spans two row-waves)
+template <int R>
+__device__ __forceinline__ int epi_slot(const EpiCtx& t, int jr) {
+  return (R > GM_WROWS ? t.base + jr : jr) & (R - 1);
+}
+
+// value of channel c of (kv or score) at wave row jr: the accumulator plus
+// a_ape (the Ape of the row's slot), or the staged row for positions before
+// the call; false if no token there
 template <int R, bool FAST>
-__device__ __forceinline__ bool epi_value(const EpiCtx& t, float a_kv, float a_z, int jr, int c,
-                                          float& kv, float& z) {
+__device__ __forceinline__ bool epi_value(const EpiCtx& t, float a_kv, float a_z, float a_ape,
+                                          int jr, int c, float& kv, float& z) {
   const int cD = t.cf.D;
-  // slot of the row in its window (the wave starts a window unless a window
-  // spans two row-waves)
-  const int q = (R > GM_WROWS ? t.base + jr : jr) & (R - 1);
   if (FAST) {
     kv = a_kv;
-    z = a_z + t.ape[q * cD + c];
+    z = a_z + a_ape;
     return true;
   }
   const int p = t.base + jr;
@@ -165,7 +171,7 @@ __device__ __forceinline__ bool epi_value(const EpiCtx& t, float a_kv, float a_z
     z = row[cD + c];
   } else {
     kv = a_kv;
-    z = a_z + t.ape[q * cD + c];
+    z = a_z + a_ape;
   }
   return z != -INFINITY;
 }
@@ -196,8 +202,11 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
           for (int q = 0; q < R; ++q) {
             const int r = 4 * rg + pw * R + q;
             const int jr = 32 * i + 8 * rg + 4 * h + pw * R + q;
-            ok[0][q] = epi_value<R, FAST>(t, acc[i][0][r], acc[i][1][r], jr, t.c0, kv[0][q], z[0][q]);
-            ok[1][q] = epi_value<R, FAST>(t, acc[i][2][r], acc[i][3][r], jr, t.c1, kv[1][q], z[1][q]);
+            const int sl = epi_slot<R>(t, jr);
+            ok[0][q] = epi_value<R, FAST>(t, acc[i][0][r], acc[i][1][r], t.ape[sl * t.cf.D + t.c0],
+                                          jr, t.c0, kv[0][q], z[0][q]);
+            ok[1][q] = epi_value<R, FAST>(t, acc[i][2][r], acc[i][3][r], t.ape[sl * t.cf.D + t.c1],
+                                          jr, t.c1, kv[1][q], z[1][q]);
           }
           const int wl = (32 * i + 8 * rg + 4 * h + pw * R) / R;   // window in the wave
 #pragma unroll
@@ -233,13 +242,24 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
         if ((32 * i + 31) / R < w || (32 * i) / R > w) continue;
         float kvb[2][16], zb[2][16];
         bool okb[2][16];
+        // the Ape of the block's rows: runs of 4 consecutive slots, one
+        // 16-byte load each from the transposed table
+        float4 ap[2][4];
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            ap[ch][g4] = *reinterpret_cast<const float4*>(
+                t.apet + (size_t)(ch ? t.c1 : t.c0) * R + epi_slot<R>(t, 32 * i + 8 * g4 + 4 * h));
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int jr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
           const bool inw = (32 * i + 8 * (r >> 2)) / R == w;
 #pragma unroll
           for (int ch = 0; ch < 2; ++ch) {
-            okb[ch][r] = inw && epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r],
+            const float4 a4 = ap[ch][r >> 2];
+            const float av = (r & 3) == 0 ? a4.x : (r & 3) == 1 ? a4.y : (r & 3) == 2 ? a4.z : a4.w;
+            okb[ch][r] = inw && epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r], av,
                                                    jr, ch ? t.c1 : t.c0, kvb[ch][r], zb[ch][r]);
           }
         }
@@ -353,7 +373,7 @@ constexpr int epilogue_barriers() { return COFF == 2 || R > GM_WROWS ? 1 : 0; }
 template <int R, int COFF, int WV>
 __device__ __forceinline__ void pool_epilogue(
     const Cfg& cf, const f32x16 (&acc)[2][4], uint8_t* xch, const PoolTile& tl,
-    const float* __restrict__ ape, const float* __restrict__ staging,
+    const float* __restrict__ ape, const float* __restrict__ apet, const float* __restrict__ staging,
     float* __restrict__ kv_state, float* __restrict__ score_state,
     const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
     float* __restrict__ pooled, int out_rows, float* __restrict__ split, uint32_t* __restrict__ err) {
@@ -555,7 +575,7 @@ __device__ __forceinline__ void pool_epilogue(
     const int g = (n0 + wn * 128) >> 7;
     const int c0 = g * 64 + lrow, c1 = c0 + 32;
     const int wbase = P0 + GM_WROWS * wm;   // position of the wave's first row
-    EpiCtx ctx{cf, wbase, s, e, live_lo, rec[PL_FIRST], stg, ape, c0, c1, h,
+    EpiCtx ctx{cf, wbase, s, e, live_lo, rec[PL_FIRST], stg, ape, apet, c0, c1, h,
                o + wbase / R - wfirst, wfirst, wend, wbase / R,
                out_rows, pooled, smem, wm, wn};
     if (P0 >= s && P0 + BM <= live_lo) {
@@ -637,7 +657,7 @@ template <int R, int COFF, int WV, int MODE>
 __device__ __forceinline__ void pool_walk(
     const Cfg& cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int T, int B,
     const int32_t* __restrict__ plan, const TileQueue& q, int xcd, int tile, int next,
-    const float* __restrict__ ape, const float* __restrict__ staging,
+    const float* __restrict__ ape, const float* __restrict__ apet, const float* __restrict__ staging,
     float* __restrict__ kv_state, float* __restrict__ score_state,
     const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
     float* __restrict__ pooled, int out_rows, float* __restrict__ split,
@@ -665,8 +685,8 @@ __device__ __forceinline__ void pool_walk(
     int taken = -1;
     if constexpr (MUL) {
       if (has_next && threadIdx.x == 0) taken = queue_take(q, xcd);
-      pool_epilogue<R, COFF, WV>(cf, acc, xch, cur, ape, staging, kv_state, score_state, kv_tab,
-                                 st_tab, pooled, out_rows, split, err);
+      pool_epilogue<R, COFF, WV>(cf, acc, xch, cur, ape, apet, staging, kv_state, score_state,
+                                 kv_tab, st_tab, pooled, out_rows, split, err);
     } else {
 #pragma unroll
       for (int i = 0; i < epilogue_barriers<R, COFF>(); ++i) asm volatile("s_barrier" ::: "memory");
@@ -701,7 +721,7 @@ template <int R, int COFF, int WV>
 __global__ __launch_bounds__(Gm<WV>::THREADS, 1) void gemm_pool_kernel(
     Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int T, int B,
     const int32_t* __restrict__ plan, int32_t* __restrict__ tiles,
-    const float* __restrict__ ape, const float* __restrict__ staging,
+    const float* __restrict__ ape, const float* __restrict__ apet, const float* __restrict__ staging,
     float* __restrict__ kv_state, float* __restrict__ score_state,
     const int32_t* __restrict__ kv_tab, const int32_t* __restrict__ st_tab,
     float* __restrict__ pooled, int out_rows, float* __restrict__ split,
@@ -720,15 +740,15 @@ __global__ __launch_bounds__(Gm<WV>::THREADS, 1) void gemm_pool_kernel(
   const int next = tile + per_wg < hi ? tile + per_wg : -1;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (Gm<WV>::COPIERS == 0) {
-    pool_walk<R, COFF, WV, GM_ALL>(cf, X, W, T, B, plan, q, xcd, tile, next, ape, staging,
+    pool_walk<R, COFF, WV, GM_ALL>(cf, X, W, T, B, plan, q, xcd, tile, next, ape, apet, staging,
                                    kv_state, score_state, kv_tab, st_tab, pooled, out_rows, split,
                                    err, smem, wave);
   } else if (wave >= WV) {
-    pool_walk<R, COFF, WV, GM_COPY>(cf, X, W, T, B, plan, q, xcd, tile, next, ape, staging,
+    pool_walk<R, COFF, WV, GM_COPY>(cf, X, W, T, B, plan, q, xcd, tile, next, ape, apet, staging,
                                     kv_state, score_state, kv_tab, st_tab, pooled, out_rows, split,
                                     err, smem, wave - WV);
   } else {
-    pool_walk<R, COFF, WV, GM_MFMA>(cf, X, W, T, B, plan, q, xcd, tile, next, ape, staging,
+    pool_walk<R, COFF, WV, GM_MFMA>(cf, X, W, T, B, plan, q, xcd, tile, next, ape, apet, staging,
                                     kv_state, score_state, kv_tab, st_tab, pooled, out_rows, split,
                                     err, smem, wave);
   }

@@ -6,16 +6,19 @@
 namespace cmp {
 
 // ---------------------------------------------------------------------------
-// Setup of a prefill call: one launch of three independent parts.
+// Setup of a prefill call: one launch of four independent parts.
 //  * workgroup 0 plans the call (per-request start, length, windows, output
 //    rows and GEMM tiles), writes the call's error word and clears the
 //    GEMM's tile queue heads;
 //  * the next D*D/2048 workgroups (rotate only) check the Hadamard matrix
 //    and copy it to the MFMA fragment order;
+//  * for ratios of 8 and more, R/4 workgroups copy Ape transposed
+//    ([channel][slot]), so that the GEMM epilogue reads the Ape of 4
+//    consecutive slots with one load;
 //  * the rest stage the ring rows of positions before each request's first
 //    token (read once here, before the GEMM stores any state row).
 // No part reads another's output, so they need no ordering inside the
-// launch; every later kernel of the call sees all three.
+// launch; every later kernel of the call sees all four.
 // ---------------------------------------------------------------------------
 constexpr int SETUP_THREADS = 256;
 
@@ -480,12 +483,28 @@ __device__ __forceinline__ void prefix_block(const Cfg& cf, int j, int b, int B,
 // The setup launch: workgroup 0 plans, workgroups [1, 1 + nhad) pack the
 // Hadamard matrix (nhad = 0 without rotate), the rest stage ring rows,
 // coff*r per request.
+// Slots 4j .. 4j+3 of Ape (fp32 [ratio, coff*D], coff = 1 here) into
+// apet[c][4j .. 4j+3] for every channel c.
+__device__ __forceinline__ void ape_transpose_block(const Cfg& cf, int j, const float* __restrict__ ape,
+                                                    float* __restrict__ apet) {
+  const int cD = cf.coff * cf.D;
+  for (int c = threadIdx.x; c < cD; c += SETUP_THREADS) {
+    float4 v;
+    v.x = ape[(size_t)(4 * j + 0) * cD + c];
+    v.y = ape[(size_t)(4 * j + 1) * cD + c];
+    v.z = ape[(size_t)(4 * j + 2) * cD + c];
+    v.w = ape[(size_t)(4 * j + 3) * cD + c];
+    *reinterpret_cast<float4*>(apet + (size_t)c * cf.ratio + 4 * j) = v;
+  }
+}
+
 __global__ __launch_bounds__(SETUP_THREADS) void setup_kernel(
     Cfg cf, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ seqused,
     const int32_t* __restrict__ start_pos, int B, int T, int out_rows,
     int32_t* __restrict__ plan, int32_t* __restrict__ tile_count, uint32_t* __restrict__ err,
     const uint16_t* __restrict__ had, uint16_t* __restrict__ hadF,
-    uint32_t* __restrict__ had_flags, int nhad, const float* __restrict__ kv_state,
+    uint32_t* __restrict__ had_flags, int nhad, const float* __restrict__ ape,
+    float* __restrict__ apet, int napet, const float* __restrict__ kv_state,
     const float* __restrict__ score_state, const int32_t* __restrict__ kv_tab,
     const int32_t* __restrict__ st_tab, float* __restrict__ staging) {
   const int g = blockIdx.x;
@@ -494,8 +513,10 @@ __global__ __launch_bounds__(SETUP_THREADS) void setup_kernel(
                tile_count, err);
   } else if (g <= nhad) {
     hadamard_pack_block(g - 1, had, hadF, cf.D, had_flags);
+  } else if (g <= nhad + napet) {
+    ape_transpose_block(cf, g - 1 - nhad, ape, apet);
   } else {
-    const int i = g - 1 - nhad, per = cf.coff * cf.ratio;
+    const int i = g - 1 - nhad - napet, per = cf.coff * cf.ratio;
     prefix_block(cf, i % per, i / per, B, T, cu_seqlens, seqused, start_pos, kv_state,
                  score_state, kv_tab, st_tab, staging);
   }

@@ -445,6 +445,7 @@ PROFILE_COMMANDS = {
               "python3 bench.py --copy-calibration",
 }
 GEMM_KERNEL = "gemm_pool_kernel"
+PROFILE_OUT = "OUT"   # placeholder for the output folder in the recorded commands
 
 
 def _find_csv(folder, suffix):
@@ -471,8 +472,8 @@ def summarize_profiles(out):
     sha = kernel_source_sha("gemm.hpp", "pool.hpp", "common.hpp")
     rows = list(csv.DictReader(open(_find_csv(os.path.join(out, "kt"), "kernel_stats.csv"))))
     lines = ["# Kernel-time summary: bench.py (128K C4A prefill + 32-request decode)", "",
-             "Command (from the repository root, on one MI355X):", "", "```",
-             PROFILE_COMMANDS["kt"].format(out="gpurun_out"), "```", "",
+             "Command (from the repository root, on one MI355X; OUT is the folder for the CSV files):", "", "```",
+             PROFILE_COMMANDS["kt"].format(out=PROFILE_OUT), "```", "",
              "The 128K C4A prefill kernels run 35 times (15 warm-up + 20 timed, the timed "
              "ones with per-kernel events); the other prefill workloads run before it ("
              + ", ".join(f"{n}: {OTHER_WARMUP} warm-up + {k} timed" for n, k in OTHER_PREFILL)
@@ -537,7 +538,7 @@ def summarize_profiles(out):
         "fetch_bytes_per_launch": fb,
         "write_bytes_per_launch": wb,
         "hbm_bytes_per_launch": fb + wb,
-        "commands": [PROFILE_COMMANDS[k].format(out="gpurun_out")
+        "commands": [PROFILE_COMMANDS[k].format(out=PROFILE_OUT)
                      for k in ("fetch", "write", "cfetch", "cwrite")],
     }
     json.dump(doc, open(os.path.join(ROOT, "profiles", "gemm_c4a_128k_traffic.json"), "w"),
@@ -570,8 +571,8 @@ def summarize_mfma(out, sha):
     # the 128K launches are the ones with the call's full MFMA work
     rows = [d for d in rows if abs(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 - flops) < 1e-3 * flops]
     lines = ["# 128K C4A prefill GEMM: clock and matrix-core busy cycles", "",
-             "Command (from the repository root, on one MI355X):", "", "```",
-             PROFILE_COMMANDS["mfma"].format(out="gpurun_out"), "```", "",
+             "Command (from the repository root, on one MI355X; OUT is the folder for the CSV files):", "", "```",
+             PROFILE_COMMANDS["mfma"].format(out=PROFILE_OUT), "```", "",
              "Per launch of `gemm_pool_kernel` (15 warm-up + 10 timed, in launch order). "
              "clock = GRBM_GUI_ACTIVE / 8 XCCs / duration; MFMA busy = "
              "SQ_VALU_MFMA_BUSY_CYCLES / (GUI-active cycles per XCC x 1024 SIMDs); "
@@ -621,8 +622,8 @@ def summarize_decode(out, fscale, wscale):
         return {order[0]: rows[:h], order[1]: rows[h:]}
 
     lines = ["# Decode kernels: 32-request step, H = 7168, D = 512", "",
-             "Commands (from the repository root, on one MI355X):", "", "```"]
-    lines += [PROFILE_COMMANDS[k].format(out="gpurun_out") for k in ("dkt", "dfetch", "dwrite",
+             "Commands (from the repository root, on one MI355X; OUT is the folder for the CSV files):", "", "```"]
+    lines += [PROFILE_COMMANDS[k].format(out=PROFILE_OUT) for k in ("dkt", "dfetch", "dwrite",
                                                                     "cfetch", "cwrite")]
     lines += ["```", "",
               "Durations from the kernel trace (every launch of the run: eager, graph-replayed "

@@ -66,10 +66,11 @@ def bench_prefill(steps, warmup, name="c4a_128k", prepared=None):
     for _ in range(warmup):
         case.prefill()
     torch.cuda.synchronize()
-    # the timed steps themselves give the per-kernel durations: while timing
-    # is on, the library brackets every launch with HIP events on the stream
-    # it launches on (about 0.5% on the 128K call's time, included in it)
-    cmp.compressor_timing_enable(True)
+    # the timed steps themselves give the projection GEMM's duration: in
+    # timing mode 2 the library brackets each GEMM launch with HIP events on
+    # the stream it launches on (the overhead, ~0.1% of the 128K call, is
+    # included in its time)
+    cmp.compressor_timing_enable(2)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record()
     for i in range(steps):
@@ -78,13 +79,20 @@ def bench_prefill(steps, warmup, name="c4a_128k", prepared=None):
     torch.cuda.synchronize()
     total_ms = evs[0].elapsed_time(evs[-1])
     per_call = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
-    kernels = {}
-    for k in ("setup", "gemm", "post"):
+    n, ms = cmp.compressor_timing_query("gemm")
+    assert n == steps, (n, steps)
+    kernels = {"gemm": ms / n}
+    # the other kernels' durations: a short pass after the timed steps with
+    # every launch bracketed
+    cmp.compressor_timing_enable(1)
+    for _ in range(KERNEL_PASS):
+        case.prefill()
+    torch.cuda.synchronize()
+    for k in ("setup", "post"):
         n, ms = cmp.compressor_timing_query(k)
         if n:
-            assert n == steps, (k, n, steps)
             kernels[k] = ms / n
-    cmp.compressor_timing_enable(False)
+    cmp.compressor_timing_enable(0)
     windows = w["T"] // w["ratio"]
     out_bits = case.out_bits().copy()
     kv, sc = case.states()
@@ -417,6 +425,7 @@ def parity_stats(pre, res, rows):
 # the secondary prefill workloads (timed steps each) and their warm-up calls
 OTHER_PREFILL = (("c128a_8192", 200), ("varlen_c4a", 100))
 OTHER_WARMUP = 10
+KERNEL_PASS = 5      # calls of the per-kernel pass after each prefill's timed steps
 
 PROFILE_COMMANDS = {
     "kt": "rocprofv3 --kernel-trace --stats -T --output-format csv -d {out}/kt -o run -- "
@@ -474,9 +483,10 @@ def summarize_profiles(out):
     lines = ["# Kernel-time summary: bench.py (128K C4A prefill + 32-request decode)", "",
              "Command (from the repository root, on one MI355X; OUT is the folder for the CSV files):", "", "```",
              PROFILE_COMMANDS["kt"].format(out=PROFILE_OUT), "```", "",
-             "The 128K C4A prefill kernels run 35 times (15 warm-up + 20 timed, the timed "
-             "ones with per-kernel events); the other prefill workloads run before it ("
-             + ", ".join(f"{n}: {OTHER_WARMUP} warm-up + {k} timed" for n, k in OTHER_PREFILL)
+             f"The 128K C4A prefill kernels run 15 + 20 + {KERNEL_PASS} times (15 warm-up, 20 "
+             "timed with events around each GEMM launch, then a short pass with events around "
+             "every launch); the other prefill workloads run before it ("
+             + ", ".join(f"{n}: {OTHER_WARMUP} + {k} + {KERNEL_PASS}" for n, k in OTHER_PREFILL)
              + "); the decode kernels run for each decode workload x (warm-up + timed + "
              "event-timed) steps.  Durations in ns.", "",
              "| kernel | calls | total ns | average ns | % | min ns | max ns |",
@@ -495,24 +505,25 @@ def summarize_profiles(out):
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
     # the other prefill workloads run first; the command's 128K C4A launches
-    # come last: 15 warm-up and 20 timed (the launches bench.py's roofline
-    # times)
-    n_head = 15 + 20
-    n_other = [OTHER_WARMUP + k for _, k in OTHER_PREFILL]
+    # come last: 15 warm-up, 20 timed (the launches bench.py's roofline
+    # times) and the short per-kernel pass
+    n_head = 15 + 20 + KERNEL_PASS
+    n_other = [OTHER_WARMUP + k + KERNEL_PASS for _, k in OTHER_PREFILL]
     if len(dur) == n_head + sum(n_other):
         head = dur[-n_head:]
         lines += ["", f"`{GEMM_KERNEL}` per launch of the 128K C4A prefill (ms, from the kernel "
                   "trace, in launch order): " + ", ".join(f"{x:.3f}" for x in head) + ".",
                   f"Average of the 20 timed launches (after the 15 warm-up ones): "
-                  f"{np.mean(head[15:]):.3f} ms; median {np.median(head[15:]):.3f} ms."]
+                  f"{np.mean(head[15:35]):.3f} ms; median {np.median(head[15:35]):.3f} ms."]
         at = 0
         for (name, k), n in zip(OTHER_PREFILL, n_other):
             d = dur[at:at + n]
             at += n
+            t = d[OTHER_WARMUP:OTHER_WARMUP + k]
             lines += ["", f"`{GEMM_KERNEL}` of {name}: first {OTHER_WARMUP} launches (ms) "
                       + ", ".join(f"{x:.3f}" for x in d[:OTHER_WARMUP])
-                      + f"; the {k} timed launches: median {np.median(d[OTHER_WARMUP:]):.4f} ms, "
-                      f"min {np.min(d[OTHER_WARMUP:]):.4f}, max {np.max(d[OTHER_WARMUP:]):.4f}."]
+                      + f"; the {k} timed launches: median {np.median(t):.4f} ms, "
+                      f"min {np.min(t):.4f}, max {np.max(t):.4f}."]
     lines += ["", f"Kernel source hash (gemm.hpp + pool.hpp + common.hpp): `{sha}`."]
     open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w").write("\n".join(lines) + "\n")
 
@@ -573,7 +584,8 @@ def summarize_mfma(out, sha):
     lines = ["# 128K C4A prefill GEMM: clock and matrix-core busy cycles", "",
              "Command (from the repository root, on one MI355X; OUT is the folder for the CSV files):", "", "```",
              PROFILE_COMMANDS["mfma"].format(out=PROFILE_OUT), "```", "",
-             "Per launch of `gemm_pool_kernel` (15 warm-up + 10 timed, in launch order). "
+             f"Per launch of `gemm_pool_kernel` (15 warm-up, 10 timed, {KERNEL_PASS} in the per-kernel "
+             "pass, in launch order). "
              "clock = GRBM_GUI_ACTIVE / 8 XCCs / duration; MFMA busy = "
              "SQ_VALU_MFMA_BUSY_CYCLES / (GUI-active cycles per XCC x 1024 SIMDs); "
              "MFMA work = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flop.", "",

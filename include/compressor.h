@@ -289,9 +289,11 @@ const char* compressor_status_str(int status);
  * Not ordered with calls already running on other threads. */
 int compressor_set_prefill_tile_rows(int32_t rows);
 
-/* Kernel timing: while enabled, every kernel the library enqueues is
- * bracketed by a pair of HIP events on the same stream.  Enabling clears the
- * records.  Kernel names: "setup" (request plan, Hadamard check and packing,
+/* Kernel timing: on = 1 brackets every kernel the library enqueues with a
+ * pair of HIP events on the same stream; on = 2 only the projection GEMM
+ * launches ("gemm"), for timing it inside a loop of calls with the least
+ * overhead; on = 0 stops recording (other values: CMP_ERR_INVALID).  Every
+ * call clears the records.  Kernel names: "setup" (request plan, Hadamard check and packing,
  * staging of earlier positions' ring rows), "gemm" (projection with the window
  * pooling and state stores in its epilogue), "post",
  * "decode_main" (GEMV and ring pre-pooling),

@@ -252,8 +252,10 @@ def compressor_set_prefill_tile_rows(rows: int) -> None:
     _check("compressor_set_prefill_tile_rows", library().compressor_set_prefill_tile_rows(int(rows)))
 
 
-def compressor_timing_enable(on: bool) -> None:
-    _check("compressor_timing_enable", library().compressor_timing_enable(int(bool(on))))
+def compressor_timing_enable(on) -> None:
+    """True / 1: time every launch; 2: only the projection GEMM; False / 0: stop."""
+    mode = 1 if on is True else int(on)
+    _check("compressor_timing_enable", library().compressor_timing_enable(mode))
 
 
 def compressor_timing_query(kernel: str):

@@ -33,7 +33,7 @@ struct TimedLaunch {
 };
 struct Timing {
   std::mutex mu;
-  bool on = false;
+  int on = 0;                       // 0 off, 1 every launch, 2 the projection GEMM only
   std::vector<TimedLaunch> recs;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> spare;
 } g_timing;
@@ -44,7 +44,7 @@ int launch(const char* name, hipStream_t stream, F&& fn) {
   bool timed = false;
   {
     std::lock_guard<std::mutex> lk(g_timing.mu);
-    if (g_timing.on) {
+    if (g_timing.on == 1 || (g_timing.on == 2 && std::strcmp(name, "gemm") == 0)) {
       if (!g_timing.spare.empty()) {
         a = g_timing.spare.back().first;
         b = g_timing.spare.back().second;
@@ -568,7 +568,8 @@ int compressor_timing_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_timing.mu);
   for (auto& r : g_timing.recs) g_timing.spare.push_back({r.start, r.stop});
   g_timing.recs.clear();
-  g_timing.on = on != 0;
+  if (on < 0 || on > 2) return CMP_ERR_INVALID;
+  g_timing.on = on;
   return CMP_OK;
 }
 

@@ -100,6 +100,9 @@ def test_null_arguments_rejected_before_any_launch():
     ms = ctypes.c_double()
     assert lib.compressor_timing_query(b"gemm", ctypes.byref(n), ctypes.byref(ms)) == 0
     assert n.value == 0
+    # timing modes: 0 off, 1 every launch, 2 the projection GEMM only
+    for mode, status in ((2, 0), (1, 0), (0, 0), (3, 2), (-1, 2)):
+        assert lib.compressor_timing_enable(mode) == status, mode
 
 
 def test_nsa_shape_checks_before_any_launch():

@@ -230,9 +230,12 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
   } else {
     // R >= 8: wave window w holds blocks i and runs rg with
     // (32 i + 8 rg) / R == w, in both lane halves.  Statistics one 32-row
-    // block at a time (max, then exponentials, of the block's rows in this
-    // lane), merged into the window's; each block's loads are fenced below
-    // the previous block's, so few values are live at once.
+    // block and one channel at a time (max, then exponentials, of the
+    // block's rows in this lane), merged into the window's.  Both passes
+    // read the accumulators (or, for positions before the call, the staged
+    // rows) again instead of copying the block's values: the accumulators
+    // stay live anyway, and a copy of 32 values per channel beside them
+    // spilled.
     constexpr int NW = R <= GM_WROWS ? GM_WROWS / R : 1;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -240,47 +243,48 @@ __device__ __forceinline__ void epilogue_coff1(const EpiCtx& t, const f32x16 (&a
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         if ((32 * i + 31) / R < w || (32 * i) / R > w) continue;
-        float kvb[2][16], zb[2][16];
-        bool okb[2][16];
-        // the Ape of the block's rows: runs of 4 consecutive slots, one
-        // 16-byte load each from the transposed table
-        float4 ap[2][4];
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4)
-            ap[ch][g4] = *reinterpret_cast<const float4*>(
-                t.apet + (size_t)(ch ? t.c1 : t.c0) * R + epi_slot<R>(t, 32 * i + 8 * g4 + 4 * h));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jr = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool inw = (32 * i + 8 * (r >> 2)) / R == w;
-#pragma unroll
-          for (int ch = 0; ch < 2; ++ch) {
-            const float4 a4 = ap[ch][r >> 2];
-            const float av = (r & 3) == 0 ? a4.x : (r & 3) == 1 ? a4.y : (r & 3) == 2 ? a4.z : a4.w;
-            okb[ch][r] = inw && epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r], av,
-                                                   jr, ch ? t.c1 : t.c0, kvb[ch][r], zb[ch][r]);
-          }
-        }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
+          const int c = ch ? t.c1 : t.c0;
+          // the Ape of the block's rows: runs of 4 consecutive slots, one
+          // 16-byte load each from the transposed table
+          float4 ap[4];
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            ap[g4] = *reinterpret_cast<const float4*>(
+                t.apet + (size_t)c * R + epi_slot<R>(t, 32 * i + 8 * g4 + 4 * h));
           float m = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) if (okb[ch][r]) m = fmaxf(m, zb[ch][r]);
+          for (int r = 0; r < 16; ++r) {
+            if ((32 * i + 8 * (r >> 2)) / R != w) continue;
+            const float4 a4 = ap[r >> 2];
+            const float av = (r & 3) == 0 ? a4.x : (r & 3) == 1 ? a4.y : (r & 3) == 2 ? a4.z : a4.w;
+            float kv, z;
+            if (epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r], av,
+                                   32 * i + 8 * (r >> 2) + 4 * h + (r & 3), c, kv, z))
+              m = fmaxf(m, z);
+          }
           Soft blk{m, 0.f, 0.f};
           if (m != -INFINITY) {
+            // staged rows are loaded again rather than kept live
+            if constexpr (!FAST) asm volatile("" ::: "memory");
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              if (!okb[ch][r]) continue;
-              const float pe = __builtin_amdgcn_exp2f((zb[ch][r] - m) * kLog2e);
+              if ((32 * i + 8 * (r >> 2)) / R != w) continue;
+              const float4 a4 = ap[r >> 2];
+              const float av = (r & 3) == 0 ? a4.x : (r & 3) == 1 ? a4.y : (r & 3) == 2 ? a4.z : a4.w;
+              float kv, z;
+              if (!epi_value<R, FAST>(t, acc[i][2 * ch][r], acc[i][2 * ch + 1][r], av,
+                                      32 * i + 8 * (r >> 2) + 4 * h + (r & 3), c, kv, z))
+                continue;
+              const float pe = __builtin_amdgcn_exp2f((z - m) * kLog2e);
               blk.l += pe;
-              blk.x = fmaf(pe, kvb[ch][r], blk.x);
+              blk.x = fmaf(pe, kv, blk.x);
             }
           }
           st[ch] = soft_merge(st[ch], blk);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
       // the low half needs the high half's c0 rows, the high half the low
       // half's c1 rows

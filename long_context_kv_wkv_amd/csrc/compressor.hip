@@ -258,13 +258,17 @@ int ensure_lds_limits() {
                                                   Gm<4>::LDS_BYTES);
         if (e1 == hipSuccess) e1 = e8 != hipSuccess ? e8 : e4;
       });
-    hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(post_kernel<8>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        POST_ROWS * 512 * 2);
-    hipError_t e3 = hipFuncSetAttribute(reinterpret_cast<const void*>(post_kernel<2>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        POST_ROWS * 128 * 2);
-    status = e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3);
+    const void* posts[4] = {reinterpret_cast<const void*>(post_kernel<8, 32>),
+                            reinterpret_cast<const void*>(post_kernel<8, 16>),
+                            reinterpret_cast<const void*>(post_kernel<2, 32>),
+                            reinterpret_cast<const void*>(post_kernel<2, 16>)};
+    hipError_t e2 = hipSuccess;
+    for (int i = 0; i < 4; ++i) {
+      const hipError_t e = hipFuncSetAttribute(posts[i], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               POST_ROWS * (i < 2 ? 512 : 128) * 2);
+      if (e2 == hipSuccess) e2 = e;
+    }
+    status = e1 != hipSuccess ? e1 : e2;
   });
   return status == hipSuccess ? CMP_OK : CMP_ERR_HIP;
 }
@@ -511,21 +515,20 @@ int compressor_prefill(const compressor_shape* shape, const compressor_args* a, 
     }));
   }
   if (a->out_rows > 0) {
-    const dim3 qg((a->out_rows + POST_ROWS - 1) / POST_ROWS);
+    // 16-row workgroups when 32-row ones would not give every CU one
+    const bool short_call = (a->out_rows + POST_ROWS - 1) / POST_ROWS <= device_cu_count();
+    const int pr = short_call ? 16 : POST_ROWS;
+    const dim3 qg((a->out_rows + pr - 1) / pr);
     const int lds = cf.rotate ? POST_ROWS * cf.D * 2 : 0;
     CMP_TRY(launch("post", st, [&] {
-      if (cf.D == 512)
-        hipLaunchKernelGGL(post_kernel<8>, qg, dim3(256), lds, st, cf, pooled, split, plan, B,
-                           a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
-                           static_cast<const uint16_t*>(a->cos),
-                           static_cast<const uint16_t*>(a->sin), hadF, had_flags, nhad,
-                           static_cast<uint16_t*>(a->out));
-      else
-        hipLaunchKernelGGL(post_kernel<2>, qg, dim3(256), lds, st, cf, pooled, split, plan, B,
-                           a->out_rows, static_cast<const uint16_t*>(a->norm_weight),
-                           static_cast<const uint16_t*>(a->cos),
-                           static_cast<const uint16_t*>(a->sin), hadF, had_flags, nhad,
-                           static_cast<uint16_t*>(a->out));
+      decltype(&post_kernel<8, 32>) kern =
+          cf.D == 512 ? (short_call ? post_kernel<8, 16> : post_kernel<8, 32>)
+                      : (short_call ? post_kernel<2, 16> : post_kernel<2, 32>);
+      hipLaunchKernelGGL(kern, qg, dim3(256), lds, st, cf, pooled, split, plan, B, a->out_rows,
+                         static_cast<const uint16_t*>(a->norm_weight),
+                         static_cast<const uint16_t*>(a->cos),
+                         static_cast<const uint16_t*>(a->sin), hadF, had_flags, nhad,
+                         static_cast<uint16_t*>(a->out));
     }));
   }
   return CMP_OK;

@@ -154,7 +154,7 @@ __device__ __forceinline__ bool row_has_window(const int32_t* __restrict__ plan,
 }
 
 // ---------------------------------------------------------------------------
-// Post-processing of 32 output rows per workgroup: RMSNorm (eps 1e-6, fp32,
+// Post-processing of PR (32 or 16) output rows per workgroup: RMSNorm (eps 1e-6, fp32,
 // times the weight), interleaved RoPE on channels [D-64, D) ([PyPTO]
 // 压缩窗口与状态更新 / 算子级辅助函数), then either the bf16 store or, with
 // rotate, out = y @ Had as a bf16 MFMA product (K = D) against the matrix in
@@ -162,8 +162,13 @@ __device__ __forceinline__ bool row_has_window(const int32_t* __restrict__ plan,
 // Pairs (2i, 2i+1) of the rotary slice rotate together: the even element with
 // cos/sin column i, the odd one with column 32 + i.
 //
-// Each wave normalises 8 rows in two batches of 4 (all loads of a batch in
-// flight before the first reduction).  When Had is a scaled Sylvester matrix
+// Each wave normalises PR / 4 rows in batches of 4 (all loads of a batch in
+// flight before the first reduction).  Calls whose 32-row grid would not
+// give every CU a workgroup take 16-row workgroups: one batch per wave, so
+// each workgroup waits for one load round after its plan lookups instead of
+// two (8192-token C128A call, 64 rows: 9.0 -> 6.8 us); with more rows than
+// that the extra workgroups' plan lookups cost more (128K C4A call, 32768
+// rows: 36.6 -> 42.6 us with 16-row workgroups).  When Had is a scaled Sylvester matrix
 // (no hadamard_pack_block flag is set) the product is the fast
 // Walsh-Hadamard transform of the fp32 row in registers (log2 D butterfly
 // stages: within a lane, then across lanes), times Had[0][0]: no matrix
@@ -174,7 +179,7 @@ __device__ __forceinline__ bool row_has_window(const int32_t* __restrict__ plan,
 // the kernel needed 384 registers per wave: one wave per SIMD, and half of
 // the workgroups of a 32768-row call waited for a second round).
 // ---------------------------------------------------------------------------
-constexpr int POST_ROWS = 32;
+constexpr int POST_ROWS = 32;                    // rows of the LDS tile (the most per workgroup)
 constexpr int POST_BATCH = 4;
 
 // N consecutive bf16 rotary columns, loaded as one piece
@@ -200,7 +205,7 @@ __device__ __forceinline__ void fwht_lanes(float (&y)[CPL], int lane) {
   for (int i = 0; i < CPL; ++i) y[i] = fmaf(sgn, y[i], lane_xor<M>(y[i]));
 }
 
-template <int CPL>
+template <int CPL, int PR>
 __global__ __launch_bounds__(256, 4) void post_kernel(
     Cfg cf, const float* __restrict__ pooled, const float* __restrict__ split,
     const int32_t* __restrict__ plan, int B, int out_rows,
@@ -209,13 +214,14 @@ __global__ __launch_bounds__(256, 4) void post_kernel(
     const uint32_t* __restrict__ had_flags, int nhad, uint16_t* __restrict__ out) {
   constexpr int D = CPL * 64;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [64][D] bf16, swizzled
-  __shared__ int32_t row_live[POST_ROWS];
+  static_assert(PR == 16 || PR == 32, "rows per workgroup");
+  __shared__ int32_t row_live[PR];
   // per row of the workgroup: bit 0 holds a window, bit 1 a window split
   // between GEMM tiles, bits 2.. that window's second tile
-  __shared__ int32_t row_info[POST_ROWS];
+  __shared__ int32_t row_info[PR];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row_base = blockIdx.x * POST_ROWS;
-  if ((int)threadIdx.x < POST_ROWS) {             // every row's plan lookup at once
+  const int row_base = blockIdx.x * PR;
+  if ((int)threadIdx.x < PR) {                    // every row's plan lookup at once
     const int row = row_base + threadIdx.x;
     int info = 0;
     const int rb = row < out_rows ? find_request(plan, B, row) : -1;
@@ -247,8 +253,8 @@ __global__ __launch_bounds__(256, 4) void post_kernel(
   const float hscale = cf.rotate ? bf2f(hadF[0]) : 0.f;   // Had[0][0]
 
 #pragma unroll 1
-  for (int bt = 0; bt < POST_ROWS / 4 / POST_BATCH; ++bt) {
-    const int lr0 = wave * (POST_ROWS / 4) + bt * POST_BATCH;
+  for (int bt = 0; bt < PR / 4 / POST_BATCH; ++bt) {
+    const int lr0 = wave * (PR / 4) + bt * POST_BATCH;
     // loads of the whole batch first (rows clamped into the buffers);
     // rope lanes also take cos/sin columns pr (even element) and half + pr
     // (odd element) of their pairs
@@ -368,12 +374,14 @@ __global__ __launch_bounds__(256, 4) void post_kernel(
   if (!cf.rotate || fwht) return;
   __syncthreads();
 
-  // out[POST_ROWS, D] = Y . Had; wave w owns output columns [w*D/4,
+  // out[PR, D] = Y . Had (one 32-row MFMA block; with PR = 16 its rows 16 ..
+  // 31 read LDS that no row of this workgroup filled and are not stored,
+  // and rows of the product do not mix); wave w owns output columns [w*D/4,
   // (w+1)*D/4), walked one 32-column block at a time (few accumulators live:
   // the kernel's register demand sets how many waves share a SIMD on every
   // path).  The tile is only read, so each block's rows go straight out: 32
   // lanes write 64 contiguous bytes of one row per store.
-  constexpr int RB = POST_ROWS / 32;        // 32-row blocks of the tile
+  constexpr int RB = POST_ROWS / 32;        // 32-row blocks of the LDS tile
   constexpr int NB = D / 128;               // 32-column blocks per wave
   constexpr int KS = D / 16;                // k-steps
   constexpr int PF = KS < 4 ? KS : 4;       // k-steps of Had fragments in flight
@@ -413,7 +421,8 @@ __global__ __launch_bounds__(256, 4) void post_kernel(
       for (int r = 0; r < 16; ++r) {
         const int lr = i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
         const int row = row_base + lr;
-        if (row < out_rows) out[(size_t)row * D + col] = row_live[lr] ? f2bf(acc[i][r]) : uint16_t(0);
+        if (lr < PR && row < out_rows)
+          out[(size_t)row * D + col] = row_live[lr] ? f2bf(acc[i][r]) : uint16_t(0);
       }
   }
 }

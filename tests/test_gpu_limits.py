@@ -98,3 +98,26 @@ def test_decode_largest_batch(harness, ratio):
     case.decode()
     torch.cuda.synchronize()
     _check(case, w, O.compressor(w), name)
+
+
+@pytest.mark.parametrize("kind", ["random_rotation", "no_rotation"])
+def test_post_rows_per_workgroup(harness, kind):
+    """9001 output rows: more than one 32-row post workgroup per CU, so the
+    post kernel runs its 32-row workgroups (shorter calls take 16-row ones,
+    which every smaller test covers); with a random rotation matrix (the
+    matrix-product path) and without rotation."""
+    rotate = kind == "random_rotation"
+    spec = workloads.Spec(f"lim_post_{kind}", ratio=4, head_dim=128, hidden=1024, rotate=rotate,
+                          block_size=16, batch=1, lengths=(36003,), start_pos=(5,),
+                          tables="perm", separate_kv_table=True, spare_blocks=2)
+    w = workloads.build(spec, workloads.SEED_BASE + 1360 + rotate)
+    if rotate:
+        rng = np.random.default_rng(workloads.SEED_BASE + 1362)
+        m = (rng.standard_normal((128, 128)) / np.sqrt(128)).astype(np.float32)
+        w = dict(w, hadamard=workloads.f32_to_bf16_bits(m))
+    assert w["out_rows"] > 32 * 256
+    _announce(f"lim_post_{kind} T={w['T']} out_rows={w['out_rows']}")
+    case = harness.DeviceCase(w)
+    case.prefill()
+    torch.cuda.synchronize()
+    _check(case, w, O.compressor(w), f"lim_post_{kind}")

@@ -228,14 +228,80 @@ def bench_reference(T=131072, H=7168, N=2048, reps=10):
     e1.record()
     torch.cuda.synchronize()
     cp_ms = e0.elapsed_time(e1) / reps
-    del src, dst
+    del dst
+    ceil = measured_ceilings(src, reps)
+    del src
     torch.cuda.empty_cache()
-    return {"torch_mm_same_shape_ms": mm_ms,
-            "torch_mm_same_shape_tflops": 2.0 * T * H * N / (mm_ms * 1e-3) / 1e12,
-            "copy_1GiB_GBps": 2.0 * (1 << 30) / (cp_ms * 1e-3) / 1e9,
-            "note": "vendor bf16 GEMM (torch.mm, hipBLASLt) of the shape x[131072, 7168] . "
-                    "W[2048, 7168]^T with bf16 output and no pooling, N(0,1) inputs; device copy "
-                    "of 1 GiB (read + write bytes)"}
+    out = {"torch_mm_same_shape_ms": mm_ms,
+           "torch_mm_same_shape_tflops": 2.0 * T * H * N / (mm_ms * 1e-3) / 1e12,
+           "copy_1GiB_GBps": 2.0 * (1 << 30) / (cp_ms * 1e-3) / 1e9,
+           "note": "vendor bf16 GEMM (torch.mm, hipBLASLt) of the shape x[131072, 7168] . "
+                   "W[2048, 7168]^T with bf16 output and no pooling, N(0,1) inputs; device copy "
+                   "of 1 GiB (read + write bytes)"}
+    out.update(ceil)
+    return out
+
+
+def measured_ceilings(buf, reps=10):
+    """The ceilings of this GPU measured by libpeak.so (csrc/peak.hip): a
+    plain bf16 MFMA loop (one 4-wave workgroup per CU, four independent
+    accumulators per wave, no memory traffic) on N(0, 1) operands, which
+    the matrix cores' power draw holds below the nominal peak, and on
+    constant operands; and a read-only stream over `buf` (1 GiB) with
+    16-byte loads."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "long_context_kv_wkv_amd", "libpeak.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    lib.peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20263)
+    seed = torch.randn(2048 * 8, device="cuda", dtype=torch.bfloat16, generator=g)
+    ones = torch.ones(2048 * 8, device="cuda", dtype=torch.bfloat16)
+    blocks, iters = cus, 40000
+    sink = torch.empty(blocks * 256, device="cuda", dtype=torch.float32)
+    word = torch.zeros(1, device="cuda", dtype=torch.int32)
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def mfma(src=seed):
+        rc = lib.peak_mfma_bf16(src.data_ptr(), sink.data_ptr(), blocks, iters, stream)
+        if rc != 0:
+            raise RuntimeError(f"peak_mfma_bf16: HIP error {rc}")
+
+    def read():
+        rc = lib.peak_stream_read(buf.data_ptr(), buf.numel(), word.data_ptr(), 8 * cus, stream)
+        if rc != 0:
+            raise RuntimeError(f"peak_stream_read: HIP error {rc}")
+
+    mfma_ms = timed(mfma, 5)
+    const_ms = timed(lambda: mfma(ones), 5)
+    read_ms = timed(read, reps)
+    mfma_flops = blocks * 4 * 4 * iters * 2.0 * 32 * 32 * 16
+    return {"mfma_loop_bf16_tflops": mfma_flops / (mfma_ms * 1e-3) / 1e12,
+            "mfma_loop_bf16_const_tflops": mfma_flops / (const_ms * 1e-3) / 1e12,
+            "stream_read_1GiB_GBps": buf.numel() / (read_ms * 1e-3) / 1e9,
+            "ceilings_note": "measured on this GPU by libpeak.so: bf16 32x32x16 MFMA loop, "
+                             "operands held in registers (one 4-wave workgroup per CU, no memory "
+                             "traffic), on N(0,1) values and on constant ones; read-only stream "
+                             "of 1 GiB"}
 
 
 def bench_epilog(steps, copies=9):
@@ -812,6 +878,10 @@ def main():
         "device": pre["device"],
     }
     result.update(extra)
+    if "reference" in extra:
+        ceil = extra["reference"]["mfma_loop_bf16_tflops"]
+        result["roofline"]["measured_ceiling"] = ceil
+        result["roofline"]["frac_of_measured_ceiling"] = achieved / ceil
     if not a.no_cpu_baseline:
         base, res, rows = cpu_baseline(w)
         result["cpu_baseline"] = base

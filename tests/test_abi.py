@@ -152,3 +152,17 @@ def test_every_decode_layout_fits_the_noalloc_scratch():
     lib = cmp.library()
     sh = cmp.make_shape(4, 512, 4096, False, 256, 8, 1)
     assert lib.compressor_decode_noalloc(ctypes.byref(sh), None, None, None) == 1
+
+
+def test_ceiling_probe_library_loads():
+    """libpeak.so (the benchmark's measured MFMA and HBM ceilings) is built
+    beside the operator library and rejects bad arguments before any launch."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_kv_wkv_amd", "libpeak.so"))
+    lib.peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_void_p]
+    assert lib.peak_mfma_bf16(None, None, 1, 2, None) != 0
+    assert lib.peak_mfma_bf16(1, 1, 1, 3, None) != 0            # odd iteration count
+    assert lib.peak_stream_read(None, 16384, None, 1, None) != 0
+    assert lib.peak_stream_read(1, 1000, 1, 1, None) != 0       # not a multiple of 16 KiB

@@ -90,12 +90,16 @@ def test_full_varlen_prefill_equals_token_by_token_decode(harness):
     g = O.bf16_to_f64(got[tt, o[tt, bb]])
     rms = np.sqrt(np.mean(a * a, axis=1, keepdims=True))
     worst = float(np.max(np.abs(a - g) / np.maximum(np.abs(a), rms)))
-    print(f"{len(tt)} windows over {steps} decode calls, max scaled difference {worst:.2e}")
+    same = int(np.all(full[plan.out0[bb] + k[tt, bb]] == got[tt, o[tt, bb]], axis=1).sum())
+    print(f"{len(tt)} windows over {steps} decode calls: {same} bit-identical to the prefill's "
+          f"rows, max scaled difference {worst:.2e}")
     assert worst <= 2e-2, worst
     # live state rows agree
     kvp, scp = case.states()
     kvd, scd = d.states()
     bs = w["block_size"]
+    sdiff = 0.0
+    nrows = 0
     for b in range(B):
         for p in O.live_positions(int(plan.start[b]), int(plan.end[b]), r, 2):
             q = p % (2 * r)
@@ -103,3 +107,9 @@ def test_full_varlen_prefill_equals_token_by_token_decode(harness):
             sb = w["state_block_table"][b, q // bs]
             assert np.allclose(kvp[kb, q % bs], kvd[kb, q % bs], rtol=1e-3, atol=1e-3)
             assert np.allclose(scp[sb, q % bs], scd[sb, q % bs], rtol=1e-3, atol=1e-3)
+            for pa, pb in ((kvp[kb, q % bs], kvd[kb, q % bs]), (scp[sb, q % bs], scd[sb, q % bs])):
+                fin = np.isfinite(pa)
+                if fin.any():
+                    sdiff = max(sdiff, float(np.max(np.abs(pa[fin].astype(np.float64) - pb[fin]))))
+            nrows += 1
+    print(f"{nrows} live state rows: max |prefill - decode| {sdiff:.2e}")

@@ -4,7 +4,8 @@ rotation, block sizes that do and do not divide the ring, padded slots,
 empty requests, separate or shared kv / score tables, prefill (continuing
 from state) and decode (one token per request, or packed steps of up to 4).
 
-Every case prints its parameters before it touches the GPU.
+Half of the prefill cases force 256-row projection tiles.  Every case
+prints its parameters before it touches the GPU.
 """
 import sys
 
@@ -18,7 +19,10 @@ from compare import assert_out, assert_states
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 96
+# cases from this index on run their prefill with 256-row projection tiles
+# (short calls otherwise take 128-row tiles)
+FORCE_256_FROM = 48
 
 
 def _announce(msg):
@@ -79,7 +83,12 @@ def test_random_configuration(harness, i):
               f"rotate={w['rotate']} bs={w['block_size']} B={w['batch']} T={w['T']}")
     case = harness.DeviceCase(w)
     if mode == "prefill":
-        case.prefill()
+        import long_context_kv_wkv_amd as cmp
+        cmp.compressor_set_prefill_tile_rows(256 if i >= FORCE_256_FROM else 0)
+        try:
+            case.prefill()
+        finally:
+            cmp.compressor_set_prefill_tile_rows(0)
     elif mode == "decode1":
         case.decode()
     else:

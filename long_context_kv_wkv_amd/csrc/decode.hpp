@@ -112,21 +112,47 @@ struct DecReq {
   int s, n, row0;
   uint32_t bad;
 };
-__device__ __forceinline__ DecReq dec_request(int b, int T, const int32_t* __restrict__ cu,
-                                              const int32_t* __restrict__ seqused,
-                                              const int32_t* __restrict__ start_pos) {
+// Checks of request b's fields (cu[b], cu[b + 1], seqused[b], start_pos[b],
+// loaded by the caller; absent arrays take their defaults here)
+__device__ __forceinline__ DecReq dec_check(int b, int T, bool has_cu, bool has_su, int c0, int c1,
+                                            int nu, int s) {
   DecReq q{0, 0, 0, 0u};
-  int c0 = b, c1 = b + 1;
-  if (cu) { c0 = cu[b]; c1 = cu[b + 1]; }
+  if (!has_cu) { c0 = b; c1 = b + 1; }
   if (c0 < 0 || c1 < c0 || c1 > T) { q.bad |= CMP_DEVERR_SEQLEN; return q; }
-  int n = seqused ? seqused[b] : c1 - c0;
+  const int n = has_su ? nu : c1 - c0;
   if (n < 0 || n > c1 - c0 || n > DEC_MAX_TOK) { q.bad |= CMP_DEVERR_SEQLEN; return q; }
-  const int s = start_pos ? start_pos[b] : 0;
   if (s < 0 || s > 0x7fffffff - DEC_MAX_TOK) { q.bad |= CMP_DEVERR_START_POS; return q; }
   q.s = s;
   q.n = n;
   q.row0 = c0;
   return q;
+}
+__device__ __forceinline__ DecReq dec_request(int b, int T, const int32_t* __restrict__ cu,
+                                              const int32_t* __restrict__ seqused,
+                                              const int32_t* __restrict__ start_pos) {
+  int c0 = 0, c1 = 0, nu = 0, s = 0;
+  if (cu) { c0 = cu[b]; c1 = cu[b + 1]; }
+  if (seqused) nu = seqused[b];
+  if (start_pos) s = start_pos[b];
+  return dec_check(b, T, cu != nullptr, seqused != nullptr, c0, c1, nu, s);
+}
+// The same for a wave-uniform b: lanes 0-3 load the four fields with one
+// vector load, so that they are in flight together (and beside the caller's
+// other vector loads) instead of in dependent scalar-cache rounds.
+__device__ __forceinline__ DecReq dec_request_wave(int b, int T, const int32_t* __restrict__ cu,
+                                                   const int32_t* __restrict__ seqused,
+                                                   const int32_t* __restrict__ start_pos) {
+  const int lane = threadIdx.x & 63;
+  const int32_t* src = nullptr;
+  if (lane == 0 && cu) src = cu + b;
+  if (lane == 1 && cu) src = cu + b + 1;
+  if (lane == 2 && seqused) src = seqused + b;
+  if (lane == 3 && start_pos) src = start_pos + b;
+  int v = 0;
+  if (src) v = *src;
+  return dec_check(b, T, cu != nullptr, seqused != nullptr, __builtin_amdgcn_readlane(v, 0),
+                   __builtin_amdgcn_readlane(v, 1), __builtin_amdgcn_readlane(v, 2),
+                   __builtin_amdgcn_readlane(v, 3));
 }
 
 // Ring pre-pooling: workgroups of the decode main kernel that pool, for each
@@ -154,7 +180,22 @@ __device__ __forceinline__ void prepool_block(const Cfg& cf, int b, int k, int s
                                               float* __restrict__ pp, int32_t* __restrict__ ppflag) {
   constexpr int NSPLIT = dec_split<R>();
   constexpr int NS = COFF * R / NSPLIT;          // slots per workgroup
-  const DecReq q = dec_request(b, T, cu, seqused, start_pos);
+  // one channel set: slot j of any window is ring slot j (the window starts
+  // at a multiple of r), so the table entries of the workgroup's slots do
+  // not depend on the position.  Lane t < NS loads slot t's entries with a
+  // vector load while the request fields come through the scalar cache, so
+  // the two are in flight together: one dependent round before the ring
+  // reads instead of two (the empty asm keeps the loads ahead of the early
+  // return).
+  int32_t ekl = 0, esl = 0;
+  if constexpr (COFF == 1) {
+    const int tl = min((int)(threadIdx.x & 63), NS - 1);
+    const long ti = (long)b * cf.stride + (sp * NS + tl) / cf.bs;
+    ekl = kv_tab[ti];
+    esl = st_tab[ti];
+  }
+  const DecReq q = dec_request_wave(b, T, cu, seqused, start_pos);
+  if constexpr (COFF == 1) asm volatile("" ::"v"(ekl), "v"(esl));
   const int s = q.s, e = q.s + q.n;
   const int w = s / R + k;
   if (q.n == 0 || w >= e / R) return;            // no k-th window in this call
@@ -172,7 +213,16 @@ __device__ __forceinline__ void prepool_block(const Cfg& cf, int b, int k, int s
     use[t] = p >= 0 && p < s;                    // this call's tokens come later
     rk[t] = 0;
     rs[t] = 0;
-    if (use[t] && (!state_row(cf, kv_tab, b, p, &rk[t]) || !state_row(cf, st_tab, b, p, &rs[t]))) {
+    bool ok;
+    if constexpr (COFF == 1) {
+      const int32_t ek = __builtin_amdgcn_readlane(ekl, t), es = __builtin_amdgcn_readlane(esl, t);
+      ok = ek >= 0 && ek < cf.nblocks && es >= 0 && es < cf.nblocks;
+      rk[t] = (long)ek * cf.bs + j % cf.bs;
+      rs[t] = (long)es * cf.bs + j % cf.bs;
+    } else {
+      ok = !use[t] || (state_row(cf, kv_tab, b, p, &rk[t]) && state_row(cf, st_tab, b, p, &rs[t]));
+    }
+    if (use[t] && !ok) {
       bad |= CMP_DEVERR_TABLE;
       use[t] = false;
     }

@@ -249,6 +249,55 @@ def test_device_error_flags_without_fault(harness):
     assert case2.device_error() == 0
 
 
+@pytest.mark.parametrize("name", ["decode_c4a_all", "decode_c128a_all"])
+def test_decode_device_errors_leave_other_requests(harness, name):
+    """Single-token decode where every request closes a window: request 3's
+    ring blocks are out of range in the table (its window's ring slots and
+    its token's slot) and request 5 has a negative start position.  The call
+    sets the table and start-position bits without a fault; every other
+    request's output row and every other ring block equal those of the clean
+    call bit for bit (request 5 is inactive, so the rows after it, and their
+    rotary rows, move up by one)."""
+    _announce(f"{name}: device errors in the pre-pooled windows")
+    w = workloads.build_named(name)
+    clean = harness.DeviceCase(w)
+    clean.decode()
+    torch.cuda.synchronize()
+    assert clean.device_error() == 0
+    tab = w["state_block_table"].copy()
+    tab[3, :] = w["num_blocks"] + 5
+    sp = w["start_pos"].copy()
+    sp[5] = -1
+    # rows after the inactive request move up by one: their rotary rows move
+    # with them, so that the rows stay bit-identical
+    cos, sin = w["cos"].copy(), w["sin"].copy()
+    cos[5:-1], sin[5:-1] = w["cos"][6:], w["sin"][6:]
+    bad = harness.DeviceCase(dict(w, state_block_table=tab, start_pos=sp, cos=cos, sin=sin))
+    bad.decode()
+    torch.cuda.synchronize()
+    code = bad.device_error()
+    assert code & 1 and code & 2, code
+    a, b = clean.out_bits(), bad.out_bits()
+    B = w["batch"]
+    for r in range(B):
+        if r in (3, 5):
+            continue
+        rb = r if r < 5 else r - 1
+        assert np.array_equal(a[r], b[rb]), r
+    assert np.all(b[B - 1:] == 0)                # the inactive request's row is not used
+    ka, sa = clean.states()
+    kb, sb = bad.states()
+    keep = np.ones(w["num_blocks"], bool)
+    keep[w["state_block_table"][[3, 5]].ravel()] = False
+    assert np.array_equal(ka[keep].view(np.uint32), kb[keep].view(np.uint32))
+    assert np.array_equal(sa[keep].view(np.uint32), sb[keep].view(np.uint32))
+    # request 3's blocks: nothing was written through the bad entries
+    k0, s0 = w["kv_state"], w["score_state"]
+    for blk in w["state_block_table"][3]:
+        assert np.array_equal(kb[blk].view(np.uint32), k0[blk].view(np.uint32))
+        assert np.array_equal(sb[blk].view(np.uint32), s0[blk].view(np.uint32))
+
+
 def test_host_side_errors(harness):
     _announce("host-side argument errors")
     import long_context_kv_wkv_amd as cmp

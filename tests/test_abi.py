@@ -166,3 +166,26 @@ def test_ceiling_probe_library_loads():
     assert lib.peak_mfma_bf16(1, 1, 1, 3, None) != 0            # odd iteration count
     assert lib.peak_stream_read(None, 16384, None, 1, None) != 0
     assert lib.peak_stream_read(1, 1000, 1, 1, None) != 0       # not a multiple of 16 KiB
+
+
+def test_c99_caller_links_and_calls_host_paths(tmp_path):
+    """tests/abi_c_check.c, compiled as C99 with warnings as errors against
+    include/*.h and linked to the built library, passes its host-only checks
+    (the prototypes and structs as a C caller sees them)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    cmp.library()                                # raises if the library is not built
+    pkg = os.path.dirname(cmp.LIB_PATH)
+    exe = str(tmp_path / "abi_c_check")
+    build = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                            "-I", os.path.join(ROOT, "include"),
+                            os.path.join(ROOT, "tests", "abi_c_check.c"),
+                            "-L", pkg, "-l:" + os.path.basename(cmp.LIB_PATH),
+                            "-Wl,-rpath," + pkg, "-o", exe], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "abi_c_check: 0 failures" in run.stdout

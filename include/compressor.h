@@ -120,8 +120,10 @@ typedef struct {
  * hadamard          (device) bf16 [D, D], required iff rotate: out = y @ hadamard.
  * sin, cos          (device) bf16 [out_rows, rope_head_dim]: row i rotates
  *                   output row i; column i drives the even element of pair i,
- *                   column rope_head_dim/2 + i the odd one.
- * out               (device) bf16 [out_rows, D].  Request b owns rows
+ *                   column rope_head_dim/2 + i the odd one.  May be NULL when
+ *                   out_rows is 0.
+ * out               (device) bf16 [out_rows, D]; may be NULL when out_rows is
+ *                   0 (the call then only updates the state).  Request b owns rows
  *                   [o_b, o_b + ceil(n_b/r)), o_b = sum of earlier requests'
  *                   counts; its k-th completed window is row o_b + k; every
  *                   other row (windows not completed, rows past the last

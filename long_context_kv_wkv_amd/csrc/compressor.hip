@@ -228,9 +228,10 @@ int check_args(const Cfg& cf, const compressor_args* a, bool decode, bool own_wo
   if (a->out_rows < 0) return CMP_ERR_OUT_ROWS;
   if (a->T > 0 && !a->x) return CMP_ERR_NULLPTR;
   if (!a->kv_state || !a->score_state || !a->state_block_table || !a->w_packed || !a->ape ||
-      !a->norm_weight || !a->out || (own_workspace && !a->workspace))
+      !a->norm_weight || (own_workspace && !a->workspace))
     return CMP_ERR_NULLPTR;
-  if (a->out_rows > 0 && (!a->sin || !a->cos)) return CMP_ERR_NULLPTR;
+  // with no output rows nothing reads the rotary tables or writes out
+  if (a->out_rows > 0 && (!a->out || !a->sin || !a->cos)) return CMP_ERR_NULLPTR;
   if (cf.rotate && !a->hadamard) return CMP_ERR_NULLPTR;
   if (decode) {
     if (!a->cu_seqlens && a->T != a->batch) return CMP_ERR_INVALID;

@@ -216,6 +216,27 @@ def test_no_tokens_only_zero_fill(harness):
     assert np.array_equal(kv, w["kv_state"]) and np.array_equal(sc, w["score_state"])
 
 
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+def test_no_tokens_no_output_rows(harness, mode):
+    """Every request empty and out_rows = 0: out, sin and cos are then NULL
+    (empty tensors) and the call succeeds, sets no error bit and changes no
+    state row."""
+    _announce(f"T == 0, out_rows == 0 ({mode})")
+    w = _varlen_small("varlen_t0r0", 10, rotate=False, B=2)
+    w = dict(w, x=np.zeros((0, w["hidden"]), np.uint16), T=0,
+             cu_seqlens=np.zeros(3, np.int32), out_rows=0,
+             cos=w["cos"][:0], sin=w["sin"][:0])
+    case = harness.DeviceCase(w)
+    if mode == "prefill":
+        case.prefill()
+    else:
+        case.decode(cu_seqlens=case.cu_seqlens)
+    torch.cuda.synchronize()
+    assert case.device_error() == 0
+    kv, sc = case.states()
+    assert np.array_equal(kv, w["kv_state"]) and np.array_equal(sc, w["score_state"])
+
+
 def test_block_size_one_and_trailing_rows(harness):
     _announce("block_size 1, extra out rows")
     spec = dataclasses.replace(workloads.VARLEN_C4A, name="bs1", block_size=1, batch=3,

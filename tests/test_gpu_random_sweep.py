@@ -19,10 +19,10 @@ from compare import assert_out, assert_states
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 96
+N_CASES = 512
 # cases from this index on run their prefill with 256-row projection tiles
 # (short calls otherwise take 128-row tiles)
-FORCE_256_FROM = 48
+FORCE_256_FROM = 256
 
 
 def _announce(msg):

@@ -201,6 +201,25 @@ int decode_run(const Cfg& cf, int ks, int nrb) {
   return nrb == 2 || steps <= 4 ? 4 : 8;
 }
 
+// Two column blocks per GEMV workgroup over the same K range (the x rows of
+// the range staged once for both): single-row-block calls with two channel
+// sets, K split so that the GEMV and side workgroups number one per CU (the
+// pair kernel's registers allow one 8-wave workgroup per CU).  At the 32-request
+// C4A step (H = 7168: 224 GEMV + 32 pre-pooling workgroups) it took 13.18 ->
+// 12.86 us per graph-replayed step against single-block workgroups (448 + 32,
+// two per CU).
+int decode_ksplit_pairs(const Cfg& cf, int side_wgs) {
+  const int ngrp = cf.N / 64, KT = cf.H / 16;
+  int ks = std::max(1, (256 - side_wgs) / ngrp);
+  ks = std::max(ks, (KT + 63) / 64);        // at most 8 k-steps per wave
+  ks = std::min(ks, KT / 32);               // at least 4 k-steps per wave
+  return std::max(1, std::min(ks, DEC_MAX_KSPLIT));
+}
+bool decode_pairs(const Cfg& cf, int nrb, int side_wgs) {
+  if (nrb != 1 || cf.coff != 2 || side_wgs >= 256) return false;
+  return decode_run(cf, decode_ksplit_pairs(cf, side_wgs), 1) == 8;
+}
+
 constexpr int kDecodeMaxBatch = 64;
 constexpr int kDecodeMaxRows = 64;       // packed x rows of a decode call
 
@@ -293,18 +312,23 @@ int decode_impl(Cfg cf, const DecodeLayout& L, const compressor_args* a, uint8_t
   const int max_tok = a->cu_seqlens ? std::min(T, DEC_MAX_TOK) : 1;
   const int nwin = std::max(1, std::min(DEC_MAX_WIN, (max_tok + cf.ratio - 1) / cf.ratio));
   const int side = B * nwin * L.split;
-  const int ks = decode_ksplit(cf, side);
-  const dim3 gg(side + cf.N / 32 * ks);
   const int nrb = T <= 32 ? 1 : 2;
+  const bool pairs = decode_pairs(cf, nrb, side);
+  const int ks = pairs ? decode_ksplit_pairs(cf, side) : decode_ksplit(cf, side);
+  const dim3 gg(side + cf.N / 32 / (pairs ? 2 : 1) * ks);
   const int run = decode_run(cf, ks, nrb);
   CMP_TRY(launch("decode_main", st, [&] {
     const uint16_t* X = static_cast<const uint16_t*>(a->x);
     const uint16_t* W = static_cast<const uint16_t*>(a->w_packed);
-    decltype(&decode_main_kernel<1, 8, 4, 2>) kern = nullptr;
+    decltype(&decode_main_kernel<1, 8, 4, 2, 1>) kern = nullptr;
     with_ratio(cf.ratio, [&]<int R>() {
       constexpr int C = coff_of<R>();
-      kern = nrb == 2 ? decode_main_kernel<2, 4, R, C>
-                      : (run == 8 ? decode_main_kernel<1, 8, R, C> : decode_main_kernel<1, 4, R, C>);
+      if constexpr (C == 2) {
+        if (pairs) { kern = decode_main_kernel<1, 8, R, C, 2>; return; }
+      }
+      kern = nrb == 2 ? decode_main_kernel<2, 4, R, C, 1>
+                      : (run == 8 ? decode_main_kernel<1, 8, R, C, 1>
+                                  : decode_main_kernel<1, 4, R, C, 1>);
     });
     hipLaunchKernelGGL(kern, gg, dim3(GV_THREADS), 0, st, cf, X, W, partial, B, T, nwin, ks,
                        a->cu_seqlens, a->seqused, a->start_pos, a->kv_state, a->score_state, kvt,

@@ -3,16 +3,18 @@
 // The projection of B <= 64 tokens streams the whole weight panel from HBM
 // once, so it is bound by HBM bandwidth, not by the matrix cores.  It is split
 // over output columns and K so that every CU streams its own slice: a
-// workgroup owns 32 panel columns and one K range that its 8 waves divide;
-// each wave multiplies its x fragments (rows = tokens) by the weight
-// fragments it loads straight from HBM with the 32x32x16 bf16 MFMA.  The 8
-// waves reduce through LDS and the workgroup writes one fp32 partial per K
-// range; the tail kernel sums the K ranges in a fixed order (deterministic).
+// workgroup owns 32 panel columns (or, for single-row-block calls with two
+// channel sets, 64: two column blocks that share the staged x rows) and one
+// K range that its 8 waves divide; each wave multiplies its x fragments
+// (rows = tokens) by the weight fragments it loads straight from HBM with the
+// 32x32x16 bf16 MFMA.  The 8 waves reduce through LDS and the workgroup
+// writes one fp32 partial per K range and column; the tail kernel sums the K
+// ranges in a fixed order (deterministic).
 //
 // The K split: the H/16 k-steps are cut into 8 * KS nearly equal wave ranges
 // (KS K ranges of 8 waves), so any H that is a multiple of 512 is covered
-// whole; KS is chosen for about 512 GEMV workgroups (two per CU) with 4 to 8
-// k-steps per wave.  All of a wave's loads are issued before its first MFMA:
+// whole; KS is chosen for about 512 single-block GEMV workgroups (two per
+// CU), or about one pair workgroup per CU, with 4 to 8 k-steps per wave.  All of a wave's loads are issued before its first MFMA:
 // with more loads in flight per wave than one round of HBM latency covers,
 // a second round per wave only adds its latency (measured: 7 steps per wave
 // over 512 workgroups streams the 29 MB C4A panel in 8.5 us of graph time
@@ -36,17 +38,18 @@ typedef __attribute__((address_space(1))) void dec_glb_t;
 // same number of loads).  The x rows of the run go to the wave's own LDS
 // region by direct-to-LDS copies that each cover whole 16-byte-chunk runs of
 // rows (a row of the run is U*32 contiguous bytes), then the panel fragments
-// of the run are loaded (1 KiB contiguous each); once the copies have
-// landed, the x fragments are read from LDS and the MFMAs run.  Row t, chunk
+// of the run are loaded (1 KiB contiguous each, for each of the CBW column
+// blocks); once the copies have landed, the x fragments are read from LDS
+// and the MFMAs run, each x fragment for all CBW blocks.  Row t, chunk
 // c sits at t*U*32 + ((c ^ (t & m)) * 16), m = min(2U, 16) - 1 (the swizzle
 // never leaves the row's 2U chunks): the fragment reads (32 rows at one
 // chunk index) spread over the banks.  Rows >= B repeat row B-1 (their
 // results are not used).  NT: the panel loads carry the non-temporal
 // (streaming) hint; every panel byte is read once per call.
-template <int U, int NRB, bool NT>
-__device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp,
+template <int U, int NRB, bool NT, int CBW = 1>
+__device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp, size_t cbstride,
                                          const uint16_t* __restrict__ xk, int K, int B, int s,
-                                         int n, uint8_t* xl, f32x16* acc) {
+                                         int n, uint8_t* xl, f32x16 (*acc)[NRB]) {
   constexpr int CPR = 2 * U;             // 16-byte chunks per row of the run
   constexpr int RPI = 64 / CPR;          // rows per copy instruction
   constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;   // chunk swizzle mask: stays inside the row
@@ -61,15 +64,21 @@ __device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp,
         (dec_glb_t*)(xk + (size_t)min(t, B - 1) * K + ks * 16 + (c & 1) * 8),
         (dec_lds_t*)(xl + j * 1024), 16, 0, 0);
   }
-  bf16x8 wf[U];
+  // the run's panel fragments of each of the CBW column blocks (cbstride
+  // elements apart)
+  bf16x8 wf[CBW][U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(wp + min(s + u, n - 1) * 512);
-    wf[u] = NT ? __builtin_nontemporal_load(src) : *src;
-  }
-  // the copies were issued first: when only the U panel loads are
+  for (int cb = 0; cb < CBW; ++cb)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bf16x8* src =
+          reinterpret_cast<const bf16x8*>(wp + cb * cbstride + min(s + u, n - 1) * 512);
+      wf[cb][u] = NT ? __builtin_nontemporal_load(src) : *src;
+    }
+  // the copies were issued first: when only the CBW * U panel loads are
   // outstanding, they have landed
-  __builtin_amdgcn_s_waitcnt((U & 0xf) | ((U >> 4) << 14) | 0x0f70);
+  constexpr int NL = CBW * U;
+  __builtin_amdgcn_s_waitcnt((NL & 0xf) | ((NL >> 4) << 14) | 0x0f70);
   __builtin_amdgcn_sched_barrier(0);
   // every MFMA runs (a branch around the steps past n would let the compiler
   // sink their panel loads into it, one round trip at a time); those steps
@@ -83,7 +92,9 @@ __device__ __forceinline__ void gemv_run(const uint16_t* __restrict__ wp,
       const int c = 2 * u + (lane >> 5);
       bf16x8 xf = *reinterpret_cast<const bf16x8*>(xl + t * CPR * 16 + ((c ^ (t & SWZ)) << 4));
       xf = s + u < n ? xf : zero;
-      acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, wf[u], acc[rb], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < CBW; ++cb)
+        acc[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, wf[cb][u], acc[cb][rb], 0, 0, 0);
     }
   }
   // the next run's copies overwrite the region: every read must be done
@@ -313,11 +324,12 @@ __device__ __forceinline__ void dec_records(const Cfg& cf, int B, const int32_t*
 // (prepool_block; nwin <= DEC_MAX_WIN is the most windows a request can
 // complete in this call); with one row per request (cu NULL) workgroup 0
 // also writes the request records.  The rest run the GEMV over the T packed
-// rows: workgroup g owns column block g % (N / 32) and K range kr =
-// g / (N / 32); wave w covers wave range 8 kr + w (dec_wave_range) in runs of
-// RUN k-steps; the 8 waves reduce through LDS in a fixed order and the
-// workgroup writes one fp32 partial per K range.
-template <int NRB, int RUN, int R, int COFF>
+// rows: workgroup g owns the CBW column blocks from CBW * (g % (N / 32 /
+// CBW)) and K range kr = g / (N / 32 / CBW); wave w covers wave range 8 kr + w
+// (dec_wave_range) in runs of RUN k-steps, the x rows of a run staged once
+// for the CBW blocks; the 8 waves reduce through LDS in a fixed order and
+// the workgroup writes one fp32 partial per K range and column.
+template <int NRB, int RUN, int R, int COFF, int CBW>
 __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
     Cfg cf, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     float* __restrict__ partial, int B, int T, int nwin, int KS,
@@ -328,7 +340,7 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
     float* __restrict__ pp, int32_t* __restrict__ ppflag, DecRec* __restrict__ rec,
     uint32_t* __restrict__ err) {
   // per wave: the x rows of a run, then (after the runs) its accumulators
-  static_assert(NRB * 32 * RUN * 32 >= NRB * 16 * 64 * 4, "the reduction fits the x region");
+  static_assert(NRB * 32 * RUN * 32 >= CBW * NRB * 16 * 64 * 4, "the reduction fits the x region");
   __shared__ __attribute__((aligned(1024))) uint8_t xstage[GV_THREADS / 64][NRB * 32 * RUN * 32];
   constexpr int NSPLIT = dec_split<R>();
   const int npre = B * nwin * NSPLIT;
@@ -343,8 +355,8 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
   }
   const int g = blockIdx.x - npre;
   const int N = cf.N, K = cf.H, KT = K >> 4;
-  const int ncb = N / 32;
-  const int cb = g % ncb, kr = g / ncb;
+  const int ncg = N / 32 / CBW;                  // groups of CBW column blocks
+  const int cb = g % ncg * CBW, kr = g / ncg;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
   if (g == 0 && tid == 0) *err = 0;   // this call's error word (only the tail sets bits)
@@ -357,33 +369,39 @@ __global__ __launch_bounds__(GV_THREADS) void decode_main_kernel(
   const uint16_t* xk = X + (size_t)k0 * 16;
   uint8_t* xl = xstage[wave];
 
-  f32x16 acc[NRB];
+  f32x16 acc[CBW][NRB];
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
+  for (int c = 0; c < CBW; ++c)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[rb][r] = 0.f;
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[c][rb][r] = 0.f;
 
   // the streaming hint on the panel loads: measured per ratio over graph
   // replays of 32-request steps, it saved 0.45-0.8 us per step with two
   // channel sets (ratio 4: one and two tokens per request, with and without
   // emitting requests) and cost 0.5 us at ratio 128 when few requests close
   // a window (the main kernel 6.2 -> 6.7 us in the trace)
-  for (int s = 0; s < n; s += RUN) gemv_run<RUN, NRB, COFF == 2>(wp, xk, K, T, s, n, xl, acc);
-  float* red = reinterpret_cast<float*>(xl);            // [NRB * 16][64] of this wave
+  for (int s = 0; s < n; s += RUN)
+    gemv_run<RUN, NRB, COFF == 2, CBW>(wp, (size_t)KT * 512, xk, K, T, s, n, xl, acc);
+  float* red = reinterpret_cast<float*>(xl);            // [CBW * NRB * 16][64] of this wave
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
+  for (int c = 0; c < CBW; ++c)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[(rb * 16 + r) * 64 + lane] = acc[rb][r];
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((c * NRB + rb) * 16 + r) * 64 + lane] = acc[c][rb][r];
   __syncthreads();
   // fixed-order sum of the 8 waves; element (reg, lane) -> (row, column)
-  for (int e = tid; e < NRB * 16 * 64; e += GV_THREADS) {
-    const int reg = e >> 6, ln = e & 63;
+  for (int e = tid; e < CBW * NRB * 16 * 64; e += GV_THREADS) {
+    const int creg = e >> 6, ln = e & 63;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < GV_THREADS / 64; ++w) v += reinterpret_cast<const float*>(xstage[w])[reg * 64 + ln];
+    for (int w = 0; w < GV_THREADS / 64; ++w) v += reinterpret_cast<const float*>(xstage[w])[creg * 64 + ln];
+    const int c = creg / (NRB * 16), reg = creg % (NRB * 16);
     const int rb = reg >> 4, r = reg & 15;
     const int row = rb * 32 + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-    const int col = cb * 32 + (ln & 31);
+    const int col = (cb + c) * 32 + (ln & 31);
     if (row < T) partial[((size_t)kr * T + row) * N + col] = v;
   }
 }

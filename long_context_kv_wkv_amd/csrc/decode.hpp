@@ -594,10 +594,25 @@ __global__ __launch_bounds__(TL_THREADS) void decode_tail_kernel(
   //    after the other), then Ape on the scores
   if (own) {
     if (packed) {
+      // up to TC tokens per round, each round's loads for exactly its tokens
+      // (one uniform branch per round: the round's loads still go out
+      // together)
 #pragma unroll
       for (int t0 = 0; t0 < DEC_MAX_TOK; t0 += TC) {
         if (t0 >= n) break;
-        dec_token_values<COFF, KSB, TC>(partial, q.row0, t0, n, T, cf.N, KS, c, kvt, zt);
+        const int m = min(TC, n - t0);
+        if (m >= TC)
+          dec_token_values<COFF, KSB, TC>(partial, q.row0, t0, n, T, cf.N, KS, c, kvt, zt);
+        else if constexpr (TC > 1) {
+          if (m == 1)
+            dec_token_values<COFF, KSB, 1>(partial, q.row0, t0, n, T, cf.N, KS, c, kvt, zt);
+          else if constexpr (TC > 2) {
+            if (m == 2)
+              dec_token_values<COFF, KSB, 2>(partial, q.row0, t0, n, T, cf.N, KS, c, kvt, zt);
+            else
+              dec_token_values<COFF, KSB, 3>(partial, q.row0, t0, n, T, cf.N, KS, c, kvt, zt);
+          }
+        }
       }
     }
 #pragma unroll

@@ -342,22 +342,25 @@ int decode_impl(Cfg cf, const DecodeLayout& L, const compressor_args* a, uint8_t
       decltype(&decode_tail_kernel<4, 2, 8>) tail = nullptr;
       with_ratio(cf.ratio, [&]<int R>() {
         constexpr int C = coff_of<R>();
-        tail = ks <= 8 ? decode_tail_kernel<R, C, 8>
+        tail = ks == 7 ? decode_tail_kernel<R, C, 7>
+               : ks <= 8 ? decode_tail_kernel<R, C, 8>
                          : (ks <= 16 ? decode_tail_kernel<R, C, 16>
-                                       : decode_tail_kernel<R, C, DEC_MAX_KSPLIT>);
+                                     : decode_tail_kernel<R, C, DEC_MAX_KSPLIT>);
       });
       hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, ks, B, T,
                          a->cu_seqlens, a->seqused, a->start_pos, a->ape, a->kv_state,
                          a->score_state, kvt, a->state_block_table, pp, ppflag, gamma, cosv,
                          sinv, had, out, a->out_rows, err, err2);
     } else {
-      // the tail loads a fixed number of K ranges (>= ks, <= DEC_MAX_KSPLIT)
+      // the tail loads a fixed number of K ranges (>= ks, <= DEC_MAX_KSPLIT;
+      // exactly 7, the split of the ratio-4 column-pair layout at H = 7168)
       decltype(&decode_tail1_kernel<4, 2, 8>) tail = nullptr;
       with_ratio(cf.ratio, [&]<int R>() {
         constexpr int C = coff_of<R>();
-        tail = ks <= 8 ? decode_tail1_kernel<R, C, 8>
+        tail = ks == 7 ? decode_tail1_kernel<R, C, 7>
+               : ks <= 8 ? decode_tail1_kernel<R, C, 8>
                          : (ks <= 16 ? decode_tail1_kernel<R, C, 16>
-                                       : decode_tail1_kernel<R, C, DEC_MAX_KSPLIT>);
+                                     : decode_tail1_kernel<R, C, DEC_MAX_KSPLIT>);
       });
       hipLaunchKernelGGL(tail, dim3(B + 1), dim3(TL_THREADS), 0, st, cf, partial, ks, B, rec,
                          a->ape, a->kv_state, a->score_state, pp, ppflag, gamma, cosv, sinv, had,

@@ -217,7 +217,10 @@ int decode_ksplit_pairs(const Cfg& cf, int side_wgs) {
 }
 bool decode_pairs(const Cfg& cf, int nrb, int side_wgs) {
   if (nrb != 1 || cf.coff != 2 || side_wgs >= 256) return false;
-  return decode_run(cf, decode_ksplit_pairs(cf, side_wgs), 1) == 8;
+  const int ks = decode_ksplit_pairs(cf, side_wgs);
+  // only when every workgroup gets a CU in the first round (H up to 8192
+  // with 32 side workgroups); otherwise single blocks, two per CU
+  return side_wgs + cf.N / 64 * ks <= 256 && decode_run(cf, ks, 1) == 8;
 }
 
 constexpr int kDecodeMaxBatch = 64;

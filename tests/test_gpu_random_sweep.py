@@ -42,7 +42,7 @@ def _draw(i):
     rng = np.random.default_rng(workloads.SEED_BASE + 900 + i)
     ratio = int(rng.choice([2, 4, 8, 16, 32, 64, 128]))
     D = int(rng.choice([128, 512]))
-    H = int(rng.choice([1024, 1536, 2048, 3072]))
+    H = int(rng.choice([1024, 1536, 2048, 3072, 4096, 7168]))
     rotate = bool(rng.integers(0, 2))
     bs = int(rng.choice([1, 3, 8, 16, 64]))
     mode = ["prefill", "decode1", "decode_packed"][i % 3]

@@ -294,8 +294,8 @@ int compressor_set_prefill_tile_rows(int32_t rows);
 /* Kernel timing: on = 1 brackets every kernel the library enqueues with a
  * pair of HIP events on the same stream; on = 2 only the projection GEMM
  * launches ("gemm"), for timing it inside a loop of calls with the least
- * overhead; on = 0 stops recording (other values: CMP_ERR_INVALID).  Every
- * call clears the records.  Kernel names: "setup" (request plan, Hadamard check and packing,
+ * overhead; on = 0 stops recording (other values: CMP_ERR_INVALID, with the
+ * mode and the records unchanged).  Every accepted call clears the records.  Kernel names: "setup" (request plan, Hadamard check and packing,
  * staging of earlier positions' ring rows), "gemm" (projection with the window
  * pooling and state stores in its epilogue), "post",
  * "decode_main" (GEMV and ring pre-pooling),

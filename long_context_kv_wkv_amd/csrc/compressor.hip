@@ -264,36 +264,41 @@ int check_args(const Cfg& cf, const compressor_args* a, bool decode, bool own_wo
   return CMP_OK;
 }
 
-// Kernels that use more than the default 64 KiB of dynamic LDS, set once per
-// process for the current device.
+// Kernels that use more than the default 64 KiB of dynamic LDS: the limit is
+// raised once per device (the first call on each device, with it current).
+static hipError_t set_lds_limits() {
+  hipError_t e1 = hipSuccess;
+  for (int r = 2; r <= 128; r *= 2)
+    with_ratio(r, [&]<int R>() {
+      const hipError_t e8 = hipFuncSetAttribute(gemm_kernel_of<R, 8>(),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                Gm<8>::LDS_BYTES);
+      const hipError_t e4 = hipFuncSetAttribute(gemm_kernel_of<R, 4>(),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                Gm<4>::LDS_BYTES);
+      if (e1 == hipSuccess) e1 = e8 != hipSuccess ? e8 : e4;
+    });
+  const void* posts[4] = {reinterpret_cast<const void*>(post_kernel<8, 32>),
+                          reinterpret_cast<const void*>(post_kernel<8, 16>),
+                          reinterpret_cast<const void*>(post_kernel<2, 32>),
+                          reinterpret_cast<const void*>(post_kernel<2, 16>)};
+  hipError_t e2 = hipSuccess;
+  for (int i = 0; i < 4; ++i) {
+    const hipError_t e = hipFuncSetAttribute(posts[i], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             POST_ROWS * (i < 2 ? 512 : 128) * 2);
+    if (e2 == hipSuccess) e2 = e;
+  }
+  return e1 != hipSuccess ? e1 : e2;
+}
 int ensure_lds_limits() {
-  static std::once_flag flag;
-  static hipError_t status = hipSuccess;
-  std::call_once(flag, [] {
-    hipError_t e1 = hipSuccess;
-    for (int r = 2; r <= 128; r *= 2)
-      with_ratio(r, [&]<int R>() {
-        const hipError_t e8 = hipFuncSetAttribute(gemm_kernel_of<R, 8>(),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  Gm<8>::LDS_BYTES);
-        const hipError_t e4 = hipFuncSetAttribute(gemm_kernel_of<R, 4>(),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  Gm<4>::LDS_BYTES);
-        if (e1 == hipSuccess) e1 = e8 != hipSuccess ? e8 : e4;
-      });
-    const void* posts[4] = {reinterpret_cast<const void*>(post_kernel<8, 32>),
-                            reinterpret_cast<const void*>(post_kernel<8, 16>),
-                            reinterpret_cast<const void*>(post_kernel<2, 32>),
-                            reinterpret_cast<const void*>(post_kernel<2, 16>)};
-    hipError_t e2 = hipSuccess;
-    for (int i = 0; i < 4; ++i) {
-      const hipError_t e = hipFuncSetAttribute(posts[i], hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               POST_ROWS * (i < 2 ? 512 : 128) * 2);
-      if (e2 == hipSuccess) e2 = e;
-    }
-    status = e1 != hipSuccess ? e1 : e2;
-  });
-  return status == hipSuccess ? CMP_OK : CMP_ERR_HIP;
+  static std::mutex mu;
+  static std::vector<char> done;                 // per device: 0 not yet, 1 set, 2 failed
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return CMP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)done.size() <= dev) done.resize(dev + 1, 0);
+  if (done[dev] == 0) done[dev] = set_lds_limits() == hipSuccess ? 1 : 2;
+  return done[dev] == 1 ? CMP_OK : CMP_ERR_HIP;
 }
 
 // One decode call on workspace ws (at least decode_layout(...).total bytes);
@@ -599,10 +604,10 @@ int compressor_last_device_error(const void* workspace, void* stream, int32_t* c
 }
 
 int compressor_timing_enable(int32_t on) {
+  if (on < 0 || on > 2) return CMP_ERR_INVALID;
   std::lock_guard<std::mutex> lk(g_timing.mu);
   for (auto& r : g_timing.recs) g_timing.spare.push_back({r.start, r.stop});
   g_timing.recs.clear();
-  if (on < 0 || on > 2) return CMP_ERR_INVALID;
   g_timing.on = on;
   return CMP_OK;
 }

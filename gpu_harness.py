@@ -79,7 +79,7 @@ class DeviceCase:
                   seqused=self.seqused, start_pos=self.start_pos, kv_block_table=self.kv_table,
                   hadamard=self.hadamard)
         kw.update(over)
-        return cmp.make_args(**kw)
+        return cmp.make_args(shape=self.shape, **kw)
 
     def prefill(self, **over):
         cmp.compressor_prefill(self.shape, self._args(False, **over))

@@ -195,9 +195,56 @@ def compressor_state_reset(shape: Shape, kv_state, score_state, kv_block_table,
         _dev(device_error, i, "device_error"), _stream(stream)))
 
 
+def check_sizes(shape: Shape, *, x, batch, kv_state, score_state, state_block_table, w_packed,
+                ape, norm_weight, sin, cos, out, cu_seqlens=None, seqused=None, start_pos=None,
+                kv_block_table=None, hadamard=None, **_) -> None:
+    """Raise ValueError unless every tensor has the size the C ABI reads or
+    writes for `shape` (the library sees plain pointers and cannot check)."""
+    r, D, H, coff = shape.ratio, shape.head_dim, shape.hidden, shape.coff
+    B = int(batch)
+    T = int(x.shape[0])
+    out_rows = int(out.shape[0])
+
+    def need(t, dims, name):
+        if t is not None and tuple(t.shape) != tuple(dims):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(dims)}")
+
+    need(x, (T, H), "x")
+    need(w_packed, (2 * coff * D, H), "w_packed")
+    need(ape, (r, coff * D), "ape")
+    need(norm_weight, (D,), "norm_weight")
+    need(out, (out_rows, D), "out")
+    if out_rows > 0:
+        need(sin, (out_rows, shape.rope_head_dim), "sin")
+        need(cos, (out_rows, shape.rope_head_dim), "cos")
+    if shape.rotate:
+        if hadamard is None:
+            raise ValueError("hadamard is required when rotate is set")
+        need(hadamard, (D, D), "hadamard")
+    pool = (shape.num_blocks, shape.block_size, coff * D)
+    need(kv_state, pool, "kv_state")
+    need(score_state, pool, "score_state")
+    for name, tab in (("state_block_table", state_block_table), ("kv_block_table", kv_block_table)):
+        if tab is not None and (tab.dim() != 2 or tab.shape[0] < B or
+                                tab.shape[1] != shape.table_stride):
+            raise ValueError(f"{name}: shape {tuple(tab.shape)}, expected "
+                             f"[>= {B}, {shape.table_stride}]")
+    need(cu_seqlens, (B + 1,), "cu_seqlens")
+    need(seqused, (B,), "seqused")
+    need(start_pos, (B,), "start_pos")
+
+
 def make_args(*, x, batch, kv_state, score_state, state_block_table, w_packed, ape, norm_weight,
               sin, cos, out, workspace, cu_seqlens=None, seqused=None, start_pos=None,
-              kv_block_table=None, hadamard=None) -> Args:
+              kv_block_table=None, hadamard=None, shape: Optional[Shape] = None) -> Args:
+    """Marshal the tensors of one call; with `shape`, their sizes are checked
+    against it first (check_sizes)."""
+    if shape is not None:
+        check_sizes(shape, x=x, batch=batch, kv_state=kv_state, score_state=score_state,
+                    state_block_table=state_block_table, w_packed=w_packed, ape=ape,
+                    norm_weight=norm_weight, sin=sin, cos=cos, out=out, cu_seqlens=cu_seqlens,
+                    seqused=seqused, start_pos=start_pos, kv_block_table=kv_block_table,
+                    hadamard=hadamard)
     bf, f, i = torch.bfloat16, torch.float32, torch.int32
     if workspace is not None and workspace.dtype != torch.uint8:
         raise ValueError("workspace must be a uint8 tensor")

@@ -189,3 +189,36 @@ def test_c99_caller_links_and_calls_host_paths(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "abi_c_check: 0 failures" in run.stdout
+
+
+def test_binding_checks_tensor_sizes_against_the_shape():
+    """make_args(shape=...) refuses tensors whose sizes differ from what the
+    C ABI reads or writes for the shape (the library sees plain pointers)."""
+    import torch
+    sh = cmp.make_shape(4, 128, 1024, True, 16, 6, 1)
+    B, T, out_rows = 2, 40, 12
+    bf, f, i = torch.bfloat16, torch.float32, torch.int32
+    good = dict(x=torch.empty(T, 1024, dtype=bf), batch=B,
+                kv_state=torch.empty(6, 16, 256), score_state=torch.empty(6, 16, 256),
+                state_block_table=torch.zeros(B, 1, dtype=i),
+                w_packed=torch.empty(512, 1024, dtype=bf), ape=torch.empty(4, 256),
+                norm_weight=torch.empty(128, dtype=bf), sin=torch.empty(out_rows, 64, dtype=bf),
+                cos=torch.empty(out_rows, 64, dtype=bf), out=torch.empty(out_rows, 128, dtype=bf),
+                cu_seqlens=torch.zeros(B + 1, dtype=i), start_pos=torch.zeros(B, dtype=i),
+                hadamard=torch.empty(128, 128, dtype=bf))
+    cmp.check_sizes(sh, **good)
+    bad_cases = {"x": torch.empty(T, 512, dtype=bf), "w_packed": torch.empty(256, 1024, dtype=bf),
+                 "ape": torch.empty(128, 256), "norm_weight": torch.empty(64, dtype=bf),
+                 "sin": torch.empty(out_rows - 1, 64, dtype=bf),
+                 "out": torch.empty(out_rows, 64, dtype=bf),
+                 "kv_state": torch.empty(5, 16, 256), "score_state": torch.empty(6, 16, 128),
+                 "state_block_table": torch.zeros(B - 1, 1, dtype=i),
+                 "kv_block_table": torch.zeros(B, 2, dtype=i),
+                 "cu_seqlens": torch.zeros(B, dtype=i), "start_pos": torch.zeros(B + 1, dtype=i),
+                 "hadamard": None}
+    for name, t in bad_cases.items():
+        with pytest.raises(ValueError):
+            cmp.check_sizes(sh, **dict(good, **{name: t}))
+    # no output rows: the rotary tables are not read
+    cmp.check_sizes(sh, **dict(good, out=torch.empty(0, 128, dtype=bf),
+                               sin=torch.empty(0, 64, dtype=bf), cos=torch.empty(0, 64, dtype=bf)))

@@ -351,6 +351,20 @@ def nsa_compress_with_cache(shape: NsaShape, *, input: torch.Tensor, weight: tor
     kernel ORs NSA_DEVERR_* bits into."""
     dt = torch.float16 if shape.dtype == NSA_F16 else torch.bfloat16
     paged = shape.layout == NSA_LAYOUT_PAGED
+    N, D, cbs = shape.head_num, shape.head_dim, shape.compress_block_size
+    B = int(slot_mapping.numel())
+    # sizes the kernel reads or writes (it sees plain pointers)
+    tok = (shape.page_block_size, N, D) if paged else (N, D)
+    if tuple(input.shape[1:]) != tok:
+        raise ValueError(f"input: shape {tuple(input.shape)}, expected [*, {', '.join(map(str, tok))}]")
+    if tuple(weight.shape) != (cbs, N):
+        raise ValueError(f"weight: shape {tuple(weight.shape)}, expected ({cbs}, {N})")
+    if tuple(output_cache.shape[1:]) != (N, D):
+        raise ValueError(f"output_cache: shape {tuple(output_cache.shape)}, expected [*, {N}, {D}]")
+    if act_seq_len.numel() != B:
+        raise ValueError("act_seq_len and slot_mapping must both have one entry per batch")
+    if paged and (block_table is None or block_table.dim() != 2 or block_table.shape[0] != B):
+        raise ValueError("block_table must be [batch, table_stride] for the paged layout")
     args = NsaArgs(_dev(input, dt, "input"), _dev(weight, dt, "weight"),
                    _dev(slot_mapping, torch.int32, "slot_mapping"),
                    _dev(act_seq_len, torch.int64, "act_seq_len"),

@@ -222,3 +222,22 @@ def test_binding_checks_tensor_sizes_against_the_shape():
     # no output rows: the rotary tables are not read
     cmp.check_sizes(sh, **dict(good, out=torch.empty(0, 128, dtype=bf),
                                sin=torch.empty(0, 64, dtype=bf), cos=torch.empty(0, 64, dtype=bf)))
+
+
+def test_nsa_binding_checks_tensor_sizes():
+    import torch
+    sh = cmp.make_nsa_shape(4, 32, 32, 16, 64, cmp.NSA_BF16, cmp.NSA_LAYOUT_PAGED)
+    bf, i = torch.bfloat16, torch.int32
+    good = dict(input=torch.empty(10, 64, 4, 32, dtype=bf), weight=torch.empty(32, 4, dtype=bf),
+                slot_mapping=torch.zeros(3, dtype=i), act_seq_len=torch.zeros(3, dtype=torch.int64),
+                output_cache=torch.empty(6, 4, 32, dtype=bf), block_table=torch.zeros(3, 2, dtype=i))
+    for name, t in (("input", torch.empty(10, 64, 4, 16, dtype=bf)),
+                    ("weight", torch.empty(16, 4, dtype=bf)),
+                    ("output_cache", torch.empty(6, 2, 32, dtype=bf)),
+                    ("act_seq_len", torch.zeros(2, dtype=torch.int64)),
+                    ("block_table", torch.zeros(2, 2, dtype=i))):
+        with pytest.raises(ValueError):
+            cmp.nsa_compress_with_cache(sh, **dict(good, **{name: t}))
+    # consistent sizes pass the size checks and then need device tensors
+    with pytest.raises(ValueError, match="device tensor"):
+        cmp.nsa_compress_with_cache(sh, **good)

@@ -5,7 +5,8 @@
   heights, continuing from state with padded slots;
 * block size 1024 (one block holds a request's whole ring and more);
 * prefill with many short requests (48, of 0 to 60 tokens: most tiles hold
-  one request's few windows, some requests are empty);
+  one request's few windows, some requests are empty), and with 600 (more
+  than the plan's 256 threads);
 * single-token decode at the largest batch (64 requests: the two-row-block
   GEMV with one row per request), half of them closing a window.
 
@@ -80,6 +81,24 @@ def test_prefill_many_short_requests(harness, ratio, tile_rows):
     case.prefill()
     torch.cuda.synchronize()
     _check(case, w, O.compressor(w), f"{name} bm{tile_rows}")
+
+
+@pytest.mark.parametrize("ratio", [4, 128])
+def test_prefill_more_requests_than_plan_threads(harness, ratio):
+    """600 requests: the plan walks them in chunks of its 256 threads with a
+    carried offset, and the staging of earlier positions runs one workgroup
+    per request and ring slot."""
+    name = f"lim_600_requests_r{ratio}"
+    spec = workloads.Spec(name, ratio=ratio, head_dim=128, hidden=1024, rotate=False,
+                          block_size=16, batch=600, lengths=("uniform", 0, 12),
+                          start_pos=("uniform", 0, 400), pad_rows=0, tables="perm",
+                          separate_kv_table=True, spare_blocks=2)
+    w = workloads.build(spec, workloads.SEED_BASE + 1380 + ratio)
+    _announce(f"{name} B=600 T={w['T']}")
+    case = harness.DeviceCase(w)
+    case.prefill()
+    torch.cuda.synchronize()
+    _check(case, w, O.compressor(w), name)
 
 
 @pytest.mark.parametrize("ratio", [4, 128])
